@@ -1,0 +1,360 @@
+"""Oracle attention: exact softmax attention, SAGE quantization and its
+attention emulation, Skip-Softmax emulation, and the timestep gate.
+
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+Layouts: Q is [B, S_q, Hq, D], K and V are [B, S_kv, Hkv, D], D = 128, with
+query head h reading KV head h // (Hq // Hkv) ("GQA native" in the backend
+table of "Diffusion Attention Backends"; consecutive grouping is the reading
+taken here).  Attention is non-causal and unmasked (TRTLLM Attention,
+"Requirements": a packed or mask-free path).
+
+Parity status:
+  exact_attention   pinned: brute force on tiny shapes, torch SDPA in float64,
+                    closed forms (constant V, Q = 0, one dominant key),
+                    permutation invariance, rows of P summing to 1.
+  k_channel_mean    pinned: closed-form error bound against the float64 mean,
+                    exact on constant channels.
+  sage_quantize     pinned: softmax invariance of the smoothing, round-trip
+                    error bounds, absmax element -> +-QMAX, zero blocks,
+                    per-block brute force on tiny inputs.
+  sage_attention    pinned: Q = 0 closed form, equality with exact attention
+                    on exactly representable inputs with P rounding off,
+                    independence of the KV tile size with P rounding off.
+  skip_attention    pinned: factor 0 equals exact attention, monotone skip
+                    sets, first tile never skipped, scalar brute force on tiny
+                    grids, dropped-mass error bound, a constructed case where
+                    every later tile is skipped.
+  skip_gate_enabled pinned: truth table.
+The constants that the pages do not fix (QMAX values, rounding mode, the 2**8
+P scale, the KV-mean summation order, tile sizes) are readings, checked only
+by the invariants above: "parity unpinned by the pages" for those constants.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .codecs import E4M3_MAX, INT8_MAX, e4m3_decode, e4m3_encode, f32, int8_code, bf16_round
+
+MEAN_CHUNK = 256
+_ROW_CHUNK_ELEMS = 1 << 25
+
+
+def _f64(x):
+    if hasattr(x, "detach"):            # a torch tensor (bfloat16 is exact in float32)
+        x = x.detach().cpu().float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _f32(x):
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().float().numpy()
+    return np.asarray(x, dtype=np.float32)
+
+
+def _shape_check(q, k, v):
+    B, Sq, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k.shape
+    if (Bk, Dk) != (B, D) or tuple(v.shape) != tuple(k.shape) or Hq % Hkv:
+        raise ValueError("bad attention shapes")
+    return B, Sq, Skv, Hq, Hkv, D
+
+
+def _round_out(o, out_dtype):
+    if out_dtype is None:
+        return o
+    if out_dtype == "bf16":
+        return bf16_round(o)
+    if out_dtype == "fp32":
+        return f32(o).astype(np.float64)
+    raise ValueError(out_dtype)
+
+
+# ----------------------------------------------------------------------------
+# Exact attention
+# ----------------------------------------------------------------------------
+
+def exact_attention(q, k, v, sm_scale, rows=None, out_dtype=None, return_probs=False):
+    """O = softmax(sm_scale * Q K^T) V per (batch, query head), in float64.
+
+    The plain definition of the fused multi-head attention that the pages'
+    dense mode computes ("TRTLLM Attention", section "Dense mode"): for each
+    query row i, s_ij = sm_scale * <q_i, k_j>, p_ij = exp(s_ij - max_j s_ij),
+    O_i = sum_j p_ij v_j / sum_j p_ij, over every key j (non-causal, no mask).
+
+    ``rows`` selects query rows (the same for every batch entry and head).
+    Returns O as [B, R, Hq, D] float64, and with ``return_probs`` also the
+    normalized probabilities [B, Hq, R, S_kv].
+    """
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    B, Sq, Skv, Hq, Hkv, D = _shape_check(qf, kf, vf)
+    G = Hq // Hkv
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    R = len(rows)
+    out = np.empty((B, R, Hq, D))
+    probs = np.empty((B, Hq, R, Skv)) if return_probs else None
+    step = max(1, _ROW_CHUNK_ELEMS // max(1, Skv))
+    for b in range(B):
+        for h in range(Hq):
+            kg, vg = kf[b, :, h // G, :], vf[b, :, h // G, :]
+            for r0 in range(0, R, step):
+                rr = rows[r0:r0 + step]
+                s = sm_scale * (qf[b, rr, h, :] @ kg.T)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                l = p.sum(axis=1, keepdims=True)
+                out[b, r0:r0 + step, h, :] = (p @ vg) / l
+                if return_probs:
+                    probs[b, h, r0:r0 + step, :] = p / l
+    out = _round_out(out, out_dtype)
+    return (out, probs) if return_probs else out
+
+
+# ----------------------------------------------------------------------------
+# SAGE quantization
+# ----------------------------------------------------------------------------
+
+def k_channel_mean(k):
+    """K-smoothing mean mu[b, g, d] over all S_kv tokens, binary32, pinned order.
+
+    The pages say only that K-smoothing is internal ("TRTLLM Attention",
+    section "SAGE quantization"; "Diffusion Attention Backends", section
+    "TRTLLM_ATTN SAGE Quantization").  Reading: subtract the per-channel mean
+    of K over every token of a (batch, KV head), which leaves softmax
+    unchanged.  Summation order (pinned so a GPU can match it bit for bit):
+    tokens are cut into chunks of 256; inside a chunk a binary32 accumulator
+    starting at +0 adds the tokens in ascending order; the chunk sums are then
+    added in ascending chunk order into a binary32 total starting at +0; the
+    mean is total / binary32(S_kv), correctly rounded.
+    """
+    kf = _f32(k)
+    B, S, H, D = kf.shape
+    nch = -(-S // MEAN_CHUNK)
+    pad = nch * MEAN_CHUNK - S
+    if pad:   # adding +0.0 to an accumulator that started at +0 changes nothing
+        kf = np.concatenate([kf, np.zeros((B, pad, H, D), np.float32)], axis=1)
+    kc = kf.reshape(B, nch, MEAN_CHUNK, H, D)
+    acc = np.zeros((B, nch, H, D), np.float32)
+    for j in range(MEAN_CHUNK):
+        acc = acc + kc[:, :, j]
+    tot = np.zeros((B, H, D), np.float32)
+    for c in range(nch):
+        tot = tot + acc[:, c]
+    return tot / np.float32(S)
+
+
+def _qmax(dtype):
+    if dtype == "int8":
+        return np.float32(INT8_MAX)
+    if dtype in ("fp8", "fp8_e4m3"):
+        return np.float32(E4M3_MAX)
+    raise ValueError(f"unsupported qk dtype {dtype!r}")
+
+
+def _encode(y, dtype):
+    return int8_code(y) if dtype == "int8" else e4m3_encode(y)
+
+
+def _decode(c, dtype):
+    return c.astype(np.float64) if dtype == "int8" else e4m3_decode(c)
+
+
+def _block_quant_head(x, blk, dtype):
+    """Per-token-block quantization of one [S, D] binary32 slice.
+
+    A block is ``blk`` consecutive tokens x all D channels (the last block
+    takes what is left).  a = max |x| over the block; scale = 1 if a == 0,
+    else binary32(a / QMAX); code = encode(binary32(x / scale)).
+    """
+    S = x.shape[0]
+    qmax = _qmax(dtype)
+    starts = np.arange(0, S, blk)
+    a = np.maximum.reduceat(np.abs(x), starts, axis=0).max(axis=1)      # [nb]
+    scale = np.where(a == 0, np.float32(1.0), a / qmax).astype(np.float32)
+    per_tok = np.repeat(scale, blk)[:S]
+    y = (x / per_tok[:, None]).astype(np.float32)
+    return _encode(y, dtype), scale
+
+
+def sage_quantize(q, k, v, qk_dtype, q_block, k_block):
+    """SAGE quantization of Q, K (smoothed) and V.
+
+    * K-smoothing: K_hat = binary32(K - mu) with mu from ``k_channel_mean``;
+      Q and V are not smoothed.
+    * Q and K_hat: one scale per token block per head, blocks of ``q_block``
+      / ``k_block`` tokens along the sequence ("VisualGen Quantized
+      Attention", section "SageAttention in the TRTLLM backend"), codes int8
+      or fp8 E4M3.
+    * V: fp8 E4M3 with one scale per (batch, KV head, channel), i.e.
+      v_block_size = 1 (same section).
+
+    Returns a dict: q_codes [B,Hq,S,D], q_scale [B,Hq,ceil(S/qb)],
+    k_codes [B,Hkv,S,D], k_scale [B,Hkv,ceil(S/kb)], v_codes [B,Hkv,S,D]
+    (uint8 E4M3), v_scale [B,Hkv,D], mu [B,Hkv,D]; codes are int8 for int8
+    and uint8 E4M3 bit patterns for fp8; scales are binary32.
+    """
+    qf, kf, vf = _f32(q), _f32(k), _f32(v)
+    B, Sq, Skv, Hq, Hkv, D = _shape_check(qf, kf, vf)
+    mu = k_channel_mean(kf)
+    cdt = np.int8 if qk_dtype == "int8" else np.uint8
+    out = {
+        "q_codes": np.empty((B, Hq, Sq, D), cdt),
+        "q_scale": np.empty((B, Hq, -(-Sq // q_block)), np.float32),
+        "k_codes": np.empty((B, Hkv, Skv, D), cdt),
+        "k_scale": np.empty((B, Hkv, -(-Skv // k_block)), np.float32),
+        "v_codes": np.empty((B, Hkv, Skv, D), np.uint8),
+        "v_scale": np.empty((B, Hkv, D), np.float32),
+        "mu": mu,
+        "qk_dtype": qk_dtype, "q_block": q_block, "k_block": k_block,
+    }
+    vmax = np.float32(E4M3_MAX)
+    for b in range(B):
+        for h in range(Hq):
+            out["q_codes"][b, h], out["q_scale"][b, h] = _block_quant_head(qf[b, :, h], q_block, qk_dtype)
+        for g in range(Hkv):
+            khat = (kf[b, :, g] - mu[b, g][None, :]).astype(np.float32)
+            out["k_codes"][b, g], out["k_scale"][b, g] = _block_quant_head(khat, k_block, qk_dtype)
+            x = vf[b, :, g]
+            a = np.abs(x).max(axis=0)
+            sv = np.where(a == 0, np.float32(1.0), a / vmax).astype(np.float32)
+            out["v_scale"][b, g] = sv
+            out["v_codes"][b, g] = e4m3_encode((x / sv[None, :]).astype(np.float32))
+    return out
+
+
+def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale=256.0,
+                   out_dtype=None):
+    """SAGE attention on quantized codes, emulated tile by tile in float64.
+
+    Both matmuls run on low-precision operands ("TRTLLM Attention", section
+    "SAGE quantization"; "VisualGen Quantized Attention", section
+    "SageAttention in the TRTLLM backend").  Readings taken where the pages
+    are silent:
+      * BMM1 scale: s_ij = sm_scale * sq(i) * sk(j) * <qc_i, kc_j>, the dot
+        exact (int8 or E4M3 codes).
+      * KV tiles of ``block_n`` keys in ascending order with an online
+        softmax: M = max_j s_ij over the tile, m' = max(m, M),
+        alpha = exp(m - m'), p_ij = exp(s_ij - m').
+      * P enters BMM2 as E4M3(2**8 * p) (``quantize_p``); the row sum l takes
+        the unrounded p: l = alpha * l + sum_j p_ij.
+      * acc_d = alpha * acc_d + sum_j p~_ij * dec(vc_jd);
+        O_id = acc_d * sv_d / (2**8 * l_i).
+    Returns O [B, R, Hq, D] (float64 unless ``out_dtype`` rounds it).
+    """
+    dt = quant["qk_dtype"]
+    qb, kb = quant["q_block"], quant["k_block"]
+    qc_all, kc_all, vc_all = quant["q_codes"], quant["k_codes"], quant["v_codes"]
+    B, Hq, Sq, D = qc_all.shape
+    Hkv, Skv = kc_all.shape[1], kc_all.shape[2]
+    G = Hq // Hkv
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    R = len(rows)
+    out = np.empty((B, R, Hq, D))
+    keys = np.arange(Skv)
+    for b in range(B):
+        for g in range(Hkv):
+            kc = _decode(kc_all[b, g], dt)
+            sk = quant["k_scale"][b, g][keys // kb].astype(np.float64)
+            vd = e4m3_decode(vc_all[b, g])
+            sv = quant["v_scale"][b, g].astype(np.float64)
+            for h in range(g * G, (g + 1) * G):
+                qc = _decode(qc_all[b, h][rows], dt)
+                sq = quant["q_scale"][b, h][rows // qb].astype(np.float64)
+                s = sm_scale * sq[:, None] * sk[None, :] * (qc @ kc.T)
+                m = np.full(R, -np.inf)
+                l = np.zeros(R)
+                acc = np.zeros((R, D))
+                for t0 in range(0, Skv, block_n):
+                    st = s[:, t0:t0 + block_n]
+                    m2 = np.maximum(m, st.max(axis=1))
+                    alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m2))
+                    p = np.exp(st - m2[:, None])
+                    pq = e4m3_decode(e4m3_encode(p_scale * p)) if quantize_p else p_scale * p
+                    l = alpha * l + p.sum(axis=1)
+                    acc = alpha[:, None] * acc + pq @ vd[t0:t0 + block_n]
+                    m = m2
+                out[b, :, h, :] = acc * sv[None, :] / (p_scale * l[:, None])
+    return _round_out(out, out_dtype)
+
+
+# ----------------------------------------------------------------------------
+# Skip-Softmax
+# ----------------------------------------------------------------------------
+
+def skip_attention(q, k, v, sm_scale, factor, block_m, block_n, qtiles=None, out_dtype=None):
+    """Skip-Softmax attention in float64, with its skipped-tile set.
+
+    The pages define the threshold as factor / seqlen (the knob to
+    kernel-argument table of "SAGE + Skip-Softmax - API Design & Test Plan",
+    Part 1 section 4) and the effect as skipping low-contribution attention
+    work ("TRTLLM Attention", section "Skip-Softmax"); the feature design doc
+    with the exact rule is not among the pages.  Reading taken (seqlen =
+    S_kv, tiles of ``block_m`` query rows x ``block_n`` keys):
+      for each (batch, head, query tile) with running maxima m_i = -inf,
+      KV tiles t = 0, 1, ... in order; M_it = max of s_ij over the tile;
+      the tile is skipped iff t > 0 and, for every valid row i,
+      exp(M_it - m_i) < lambda = factor / S_kv; otherwise m_i = max(m_i, M_it)
+      and the tile's keys join row i's key set.  O_i is exact softmax
+      attention over the kept keys only.
+    ``qtiles`` selects query tiles (default: all).  Returns (O [B, R, Hq, D]
+    for the rows of the selected tiles, skipped [B, Hq, nQT, T] bool,
+    ratio [B, Hq, nQT, T] = max_i exp(M_it - m_i) with NaN at t = 0, rows).
+    """
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    B, Sq, Skv, Hq, Hkv, D = _shape_check(qf, kf, vf)
+    G = Hq // Hkv
+    nqt = -(-Sq // block_m)
+    T = -(-Skv // block_n)
+    qtiles = np.arange(nqt) if qtiles is None else np.asarray(qtiles)
+    lam = float(factor) / Skv
+    ln_lam = math.log(lam) if lam > 0 else -math.inf
+    rows = np.concatenate([np.arange(t * block_m, min(Sq, (t + 1) * block_m)) for t in qtiles])
+    out = np.empty((B, len(rows), Hq, D))
+    skipped = np.zeros((B, Hq, len(qtiles), T), bool)
+    ratio = np.full((B, Hq, len(qtiles), T), np.nan)
+    tile_starts = np.arange(0, Skv, block_n)
+    tile_of_key = np.arange(Skv) // block_n
+    for b in range(B):
+        for h in range(Hq):
+            kg, vg = kf[b, :, h // G, :], vf[b, :, h // G, :]
+            r0 = 0
+            for qi, qt in enumerate(qtiles):
+                rr = np.arange(qt * block_m, min(Sq, (qt + 1) * block_m))
+                s = sm_scale * (qf[b, rr, h, :] @ kg.T)                  # [r, S_kv]
+                M = np.maximum.reduceat(s, tile_starts, axis=1)            # [r, T]
+                m = np.full(len(rr), -np.inf)
+                for t in range(T):
+                    if t > 0:
+                        gap = M[:, t] - m
+                        ratio[b, h, qi, t] = math.exp(gap.max())
+                        if np.all(gap < ln_lam):
+                            skipped[b, h, qi, t] = True
+                            continue
+                    m = np.maximum(m, M[:, t])
+                keep = ~skipped[b, h, qi][tile_of_key]                     # [S_kv]
+                sk = np.where(keep[None, :], s, -np.inf)
+                p = np.exp(sk - sk.max(axis=1, keepdims=True))
+                out[b, r0:r0 + len(rr), h, :] = (p @ vg) / p.sum(axis=1, keepdims=True)
+                r0 += len(rr)
+    return _round_out(out, out_dtype), skipped, ratio, rows
+
+
+def skip_gate_enabled(t, D):
+    """Host-side timestep gate: Skip-Softmax is on for a step iff t <= D.
+
+    t is the normalized denoising timestep, running from 1 (noisiest) to 0;
+    both values must be finite and in [0, 1] ("TRTLLM Attention", section
+    "Skip-Softmax", key disabled_until_timestep; the design doc's knob table
+    calls it a host-side gate with no kernel argument).
+    """
+    vals = []
+    for name, x in (("t", t), ("D", D)):
+        try:
+            xf = float(x)
+        except (TypeError, ValueError):
+            raise ValueError(f"{name} must be a real number, got {x!r}") from None
+        if not (math.isfinite(xf) and 0.0 <= xf <= 1.0):
+            raise ValueError(f"{name} must be finite and in [0, 1], got {x!r}")
+        vals.append(xf)
+    return vals[0] <= vals[1]
