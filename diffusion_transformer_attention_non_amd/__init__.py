@@ -1,0 +1,354 @@
+"""Non-causal fused attention for diffusion transformers on AMD MI355X (gfx950).
+
+Python binding of ``libditattn.so`` (C ABI in ``include/ditattn.h``).  This
+layer only marshals arguments: tensors come from PyTorch (device memory and
+the current stream); every step of the computation runs in the library's HIP
+kernels.  There is no CPU or PyTorch fallback: if the library is missing the
+calls raise.
+
+Entry points (same names as the C ABI):
+  attn_dense_bf16(q, k, v)                 dense BF16 attention
+  sage_quantize(q, k, v, recipe)           SAGE codes and scales
+  attn_sage(q, k, v, recipe)               SAGE attention
+  attn_skip_softmax(q, k, v, factor)       Skip-Softmax attention
+  SkipGate(D).enabled(t)                   host-side timestep gate
+  attention(...)                           one call that routes a DiT layer
+
+Pages followed (titles as published): "TRTLLM Attention" (vllm-omni user
+guide), "Diffusion Attention Backends", "SAGE + Skip-Softmax - API Design &
+Test Plan", "VisualGen Quantized Attention (Beta)".
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "AttnError", "SageRecipe", "SkipGate", "attn_dense_bf16", "sage_quantize",
+    "attn_sage", "attn_skip_softmax", "attention", "tile_config", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libditattn.so")
+
+ATTN_OK = 0
+_STATUS = {
+    -1: "INVALID_ARG", -2: "UNSUPPORTED_HEAD_DIM", -3: "BAD_GQA", -4: "UNSUPPORTED_RECIPE",
+    -5: "BAD_LAYOUT", -6: "BAD_THRESHOLD", -7: "WORKSPACE_TOO_SMALL", -8: "DEVICE",
+    -9: "NOT_IMPLEMENTED",
+}
+_VALIDATION = {-1, -2, -3, -4, -5, -6, -7}
+DT_BF16, DT_FP32, DT_INT8, DT_FP8 = 0, 1, 2, 3
+
+
+class AttnError(RuntimeError):
+    """A device-side failure reported by the library."""
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("S_q", ctypes.c_int64), ("S_kv", ctypes.c_int64),
+                ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+
+
+class _Recipe(ctypes.Structure):
+    _fields_ = [("qk_dtype", ctypes.c_int), ("v_dtype", ctypes.c_int), ("q_block", ctypes.c_int32),
+                ("k_block", ctypes.c_int32), ("v_block", ctypes.c_int32)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("total_bytes", ctypes.c_size_t), ("q_codes_off", ctypes.c_size_t),
+                ("k_codes_off", ctypes.c_size_t), ("v_codes_off", ctypes.c_size_t),
+                ("q_scale_off", ctypes.c_size_t), ("k_scale_off", ctypes.c_size_t),
+                ("v_scale_off", ctypes.c_size_t), ("k_mean_off", ctypes.c_size_t),
+                ("scratch_off", ctypes.c_size_t), ("s_pad", ctypes.c_int64),
+                ("n_qblk", ctypes.c_int64), ("n_kblk", ctypes.c_int64)]
+
+
+_lib_handle = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m diffusion_transformer_attention_non_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        SP, RP, LP = ctypes.POINTER(_Shape), ctypes.POINTER(_Recipe), ctypes.POINTER(_Layout)
+        sig = {
+            "attn_dense_bf16": [P, P, P, P, I, SP, F, P],
+            "attn_sage_layout_query": [SP, RP, LP],
+            "sage_quantize": [P, P, P, SP, RP, P, ctypes.c_size_t, P],
+            "attn_sage": [P, P, P, P, I, SP, RP, F, P, ctypes.c_size_t, P],
+            "attn_skip_softmax": [P, P, P, P, I, SP, F, F, P, P, P],
+            "attn_skip_gate": [F, F, ctypes.POINTER(I)],
+            "attn_tile_config": [ctypes.POINTER(I), ctypes.POINTER(I)],
+            "attn_version": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = I
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        _lib_handle = lib
+    return _lib_handle
+
+
+def _check(rc: int):
+    if rc == ATTN_OK:
+        return
+    msg = _lib().attn_last_error().decode(errors="replace")
+    name = _STATUS.get(rc, str(rc))
+    if rc in _VALIDATION:
+        raise ValueError(f"ATTN_ERR_{name}: {msg}")
+    raise AttnError(f"ATTN_ERR_{name}: {msg}")
+
+
+def tile_config():
+    """(block_m, block_n): query rows per skip decision and keys per KV tile."""
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check(_lib().attn_tile_config(ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_tensors(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, S, H, D], got {tuple(t.shape)}")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.stride(-1) != 1 and t.shape[-1] > 1:
+            raise ValueError(f"{name} must have a contiguous last (head_dim) axis")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("q and k must agree on batch and head_dim")
+
+
+def _shape(q, k, v, o=None) -> _Shape:
+    B, Sq, Hq, D = q.shape
+    _, Skv, Hkv, _ = k.shape
+    s = _Shape(B=B, S_q=Sq, S_kv=Skv, Hq=Hq, Hkv=Hkv, D=D)
+    for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o if o is not None else q)):
+        getattr(s, field)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    return s
+
+
+def _out(q, out, out_dtype):
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if out.shape != q.shape or out.device != q.device or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must match q's shape and device and be bfloat16 or float32")
+    if out.stride(-1) != 1:
+        raise ValueError("out must have a contiguous last axis")
+    return out, (DT_FP32 if out.dtype == torch.float32 else DT_BF16)
+
+
+def _scale(q, sm_scale):
+    return 1.0 / math.sqrt(q.shape[-1]) if sm_scale is None else float(sm_scale)
+
+
+def attn_dense_bf16(q, k, v, out=None, out_dtype=torch.bfloat16, sm_scale=None):
+    """Dense non-causal attention softmax(sm_scale Q K^T) V, BF16 inputs."""
+    _check_tensors(q, k, v)
+    out, odt = _out(q, out, out_dtype)
+    shape = _shape(q, k, v, out)
+    _check(_lib().attn_dense_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), odt,
+                                  ctypes.byref(shape), _scale(q, sm_scale), _stream(q)))
+    return out
+
+
+@dataclass(frozen=True)
+class SageRecipe:
+    """(qk_dtype, v_dtype, (q_block, k_block, v_block)), validated like the pages' key tables.
+
+    qk_dtype: "int8" or "fp8" / "fp8_e4m3"; v_dtype: "fp8"; q_block, k_block in
+    {1, 4, 16} tokens; v_block = 1 (one V scale per head and channel).
+    """
+    qk_dtype: str = "int8"
+    v_dtype: str = "fp8"
+    q_block: int = 1
+    k_block: int = 16
+    v_block: int = 1
+
+    def __post_init__(self):
+        if self.qk_dtype not in ("int8", "fp8", "fp8_e4m3"):
+            raise ValueError(f"qk_dtype must be 'int8' or 'fp8_e4m3', got {self.qk_dtype!r}")
+        if self.v_dtype not in ("fp8", "fp8_e4m3"):
+            raise ValueError(f"v_dtype must be 'fp8', got {self.v_dtype!r}")
+        for name in ("q_block", "k_block"):
+            if getattr(self, name) not in (1, 4, 16) or isinstance(getattr(self, name), bool):
+                raise ValueError(f"{name} must be 1, 4 or 16, got {getattr(self, name)!r}")
+        if self.v_block != 1:
+            raise ValueError("v_block must be 1 (per-channel V scale)")
+
+    @property
+    def int8(self) -> bool:
+        return self.qk_dtype == "int8"
+
+    def _c(self) -> _Recipe:
+        return _Recipe(qk_dtype=DT_INT8 if self.int8 else DT_FP8, v_dtype=DT_FP8,
+                       q_block=self.q_block, k_block=self.k_block, v_block=self.v_block)
+
+
+def _layout(q, k, v, recipe: SageRecipe):
+    shape = _shape(q, k, v)
+    lay = _Layout()
+    _check(_lib().attn_sage_layout_query(ctypes.byref(shape), ctypes.byref(recipe._c()), ctypes.byref(lay)))
+    return lay
+
+
+def sage_workspace(q, k, v, recipe: SageRecipe) -> torch.Tensor:
+    """A uint8 device buffer large enough for sage_quantize / attn_sage."""
+    lay = _layout(q, k, v, recipe)
+    return torch.empty(max(1, lay.total_bytes), dtype=torch.uint8, device=q.device)
+
+
+def sage_quantize(q, k, v, recipe: SageRecipe, workspace=None):
+    """Quantize Q, K (smoothed) and V; returns views of the codes and scales.
+
+    Keys of the result: q_codes [B,Hq,s_pad,128], k_codes [B,Hkv,s_pad,128],
+    v_codes [B,Hkv,128,s_pad] (d-major), q_scale [B,Hq,n_qblk],
+    k_scale [B,Hkv,n_kblk], v_scale [B,Hkv,128], k_mean [B,Hkv,128],
+    s_pad, workspace.  Codes are int8 (int8 recipe) or uint8 E4M3 bits.
+    """
+    _check_tensors(q, k, v)
+    lay = _layout(q, k, v, recipe)
+    if workspace is None:
+        workspace = torch.empty(max(1, lay.total_bytes), dtype=torch.uint8, device=q.device)
+    shape = _shape(q, k, v)
+    _check(_lib().sage_quantize(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(shape),
+                                ctypes.byref(recipe._c()), workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return _views(workspace, lay, q, k, recipe)
+
+
+def _views(ws, lay, q, k, recipe):
+    B, Sq, Hq, D = q.shape
+    Hkv = k.shape[2]
+    sp = lay.s_pad
+
+    def region(off, n, dtype, shape):
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return ws[off:off + nbytes].view(dtype).view(shape)
+
+    cdt = torch.int8 if recipe.int8 else torch.uint8
+    return {
+        "q_codes": region(lay.q_codes_off, B * Hq * sp * D, cdt, (B, Hq, sp, D)),
+        "k_codes": region(lay.k_codes_off, B * Hkv * sp * D, cdt, (B, Hkv, sp, D)),
+        "v_codes": region(lay.v_codes_off, B * Hkv * D * sp, torch.uint8, (B, Hkv, D, sp)),
+        "q_scale": region(lay.q_scale_off, B * Hq * lay.n_qblk, torch.float32, (B, Hq, lay.n_qblk)),
+        "k_scale": region(lay.k_scale_off, B * Hkv * lay.n_kblk, torch.float32, (B, Hkv, lay.n_kblk)),
+        "v_scale": region(lay.v_scale_off, B * Hkv * D, torch.float32, (B, Hkv, D)),
+        "k_mean": region(lay.k_mean_off, B * Hkv * D, torch.float32, (B, Hkv, D)),
+        "s_pad": sp,
+        "workspace": ws,
+    }
+
+
+def attn_sage(q, k, v, recipe: SageRecipe = SageRecipe(), out=None, out_dtype=torch.bfloat16,
+              sm_scale=None, workspace=None):
+    """SAGE attention: quantize (K-smoothing inside) then attention on the codes."""
+    _check_tensors(q, k, v)
+    out, odt = _out(q, out, out_dtype)
+    lay = _layout(q, k, v, recipe)
+    if workspace is None:
+        workspace = torch.empty(max(1, lay.total_bytes), dtype=torch.uint8, device=q.device)
+    shape = _shape(q, k, v, out)
+    _check(_lib().attn_sage(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), odt, ctypes.byref(shape),
+                            ctypes.byref(recipe._c()), _scale(q, sm_scale), workspace.data_ptr(),
+                            workspace.numel(), _stream(q)))
+    return out
+
+
+def attn_skip_softmax(q, k, v, threshold_factor, out=None, out_dtype=torch.bfloat16, sm_scale=None,
+                      return_bitmap=False, return_count=False):
+    """Skip-Softmax attention with threshold = threshold_factor / S_kv.
+
+    Returns out, or (out, extras) with extras holding "bitmap" (uint8
+    [B, Hq, ceil(S_q/block_m), ceil(S_kv/block_n)], 1 = skipped) and/or
+    "skipped" (a one-element int64 tensor) when requested.
+    """
+    _check_tensors(q, k, v)
+    out, odt = _out(q, out, out_dtype)
+    shape = _shape(q, k, v, out)
+    bm, bn = tile_config()
+    bitmap = cnt = None
+    if return_bitmap:
+        B, Sq, Hq, _ = q.shape
+        bitmap = torch.empty((B, Hq, -(-Sq // bm), -(-k.shape[1] // bn)), dtype=torch.uint8, device=q.device)
+    if return_count:
+        cnt = torch.empty(1, dtype=torch.int64, device=q.device)
+    _check(_lib().attn_skip_softmax(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), odt,
+                                    ctypes.byref(shape), _scale(q, sm_scale), float(threshold_factor),
+                                    bitmap.data_ptr() if bitmap is not None else None,
+                                    cnt.data_ptr() if cnt is not None else None, _stream(q)))
+    if not (return_bitmap or return_count):
+        return out
+    extras = {}
+    if bitmap is not None:
+        extras["bitmap"] = bitmap
+    if cnt is not None:
+        extras["skipped"] = cnt
+    return out, extras
+
+
+class SkipGate:
+    """Host-side gate: Skip-Softmax runs on a step iff its normalized timestep t <= D.
+
+    t runs from 1 (noisiest, first step) to 0; D = disabled_until_timestep in
+    [0, 1].  The gate has no kernel argument: a step it disables runs dense.
+    """
+
+    def __init__(self, disabled_until_timestep: float):
+        self.D = float(disabled_until_timestep)
+        self.enabled(1.0)   # validates D
+
+    def enabled(self, t: float) -> bool:
+        flag = ctypes.c_int()
+        _check(_lib().attn_skip_gate(float(t), self.D, ctypes.byref(flag)))
+        return bool(flag.value)
+
+
+def attention(q, k, v, *, quant: SageRecipe | None = None, skip_threshold: float | None = None,
+              gate: SkipGate | None = None, timestep: float | None = None, attn_mask=None,
+              out=None, out_dtype=torch.bfloat16, sm_scale=None):
+    """One DiT attention call: dense, SAGE, or Skip-Softmax when the gate allows.
+
+    A mask is refused: this backend only serves mask-free layers.  SAGE and
+    Skip-Softmax together are not offered by the kernels yet.
+    """
+    if attn_mask is not None:
+        raise ValueError("attention masks are not supported: this path is mask-free only")
+    use_skip = skip_threshold is not None and float(skip_threshold) > 0.0
+    if use_skip and gate is not None:
+        if timestep is None:
+            raise ValueError("a gated Skip-Softmax call needs the normalized timestep")
+        use_skip = gate.enabled(timestep)
+    if quant is not None and use_skip:
+        raise ValueError("SAGE together with Skip-Softmax is not available")
+    if quant is not None:
+        return attn_sage(q, k, v, quant, out=out, out_dtype=out_dtype, sm_scale=sm_scale)
+    if use_skip:
+        return attn_skip_softmax(q, k, v, skip_threshold, out=out, out_dtype=out_dtype, sm_scale=sm_scale)
+    return attn_dense_bf16(q, k, v, out=out, out_dtype=out_dtype, sm_scale=sm_scale)

@@ -1,0 +1,378 @@
+// C ABI of the library: argument validation, workspace layout and launches.
+// Every check runs before anything is enqueued; on failure nothing is launched
+// and the thread-local message says why.  No path falls back to another one.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/ditattn.h"
+#include "internal.h"
+
+using namespace ditattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The current device must be a gfx950 part; cached per device ordinal.
+int check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 good, -1 bad
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(ATTN_ERR_DEVICE, "no HIP device is available");
+  if (dev >= 64) return fail(ATTN_ERR_DEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(ATTN_ERR_DEVICE, "cannot query device %d", dev);
+    known[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  if (known[dev] < 0) return fail(ATTN_ERR_DEVICE, "device %d is not gfx950", dev);
+  return ATTN_OK;
+}
+
+// Pointer must be device (or managed) memory of the current device.
+int check_device_ptr(const void* p, const char* name) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ATTN_ERR_INVALID_ARG, "%s is not a HIP device pointer", name);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(ATTN_ERR_INVALID_ARG, "%s is not device memory", name);
+  int dev = -1;
+  (void)hipGetDevice(&dev);
+  if (attr.device != dev) return fail(ATTN_ERR_DEVICE, "%s lives on device %d, current device is %d", name, attr.device, dev);
+  return ATTN_OK;
+}
+
+int check_shape(const attn_shape* s) {
+  if (s == nullptr) return fail(ATTN_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 0 || s->S_q < 0 || s->S_kv < 0 || s->Hq < 0 || s->Hkv < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "negative size in shape");
+  if (s->D != kHeadDim) return fail(ATTN_ERR_UNSUPPORTED_HEAD_DIM, "head_dim %lld is not 128", (long long)s->D);
+  if (s->Hkv == 0 || s->Hq % s->Hkv != 0)
+    return fail(ATTN_ERR_BAD_GQA, "Hq=%lld is not a multiple of Hkv=%lld", (long long)s->Hq, (long long)s->Hkv);
+  if (s->S_q >= kMaxIndex || s->S_kv >= kMaxIndex || s->B * s->Hq >= kMaxIndex)
+    return fail(ATTN_ERR_INVALID_ARG, "problem too large for 32-bit tile indices");
+  const int64_t nwg = ((s->S_q + kBlockM - 1) / kBlockM) * s->Hq * s->B;
+  if (nwg >= kMaxIndex) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
+  const int64_t* strides[4] = {s->q_stride, s->k_stride, s->v_stride, s->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i) {
+      const int64_t st = strides[t][i];
+      if (st < 0 || (st & 7) != 0)
+        return fail(ATTN_ERR_BAD_LAYOUT, "%s stride[%d]=%lld must be a non-negative multiple of 8 elements",
+                    names[t], i, (long long)st);
+    }
+  return ATTN_OK;
+}
+
+bool empty(const attn_shape* s) { return s->B == 0 || s->S_q == 0 || s->Hq == 0; }
+
+int check_common(const void* q, const void* k, const void* v, const void* o, attn_dtype o_dtype,
+                 const attn_shape* shape, float sm_scale) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (o_dtype != ATTN_DTYPE_BF16 && o_dtype != ATTN_DTYPE_FP32)
+    return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be BF16 or FP32");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+    return fail(ATTN_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (empty(shape)) return ATTN_OK;
+  if (shape->S_kv == 0) return fail(ATTN_ERR_INVALID_ARG, "S_kv = 0: softmax over no keys");
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_BAD_LAYOUT, "q, k, v and o must be 16-byte aligned");
+  return ATTN_OK;
+}
+
+int check_ptrs(const void* q, const void* k, const void* v, const void* o) {
+  int rc;
+  if ((rc = check_device())) return rc;
+  if ((rc = check_device_ptr(q, "q"))) return rc;
+  if ((rc = check_device_ptr(k, "k"))) return rc;
+  if ((rc = check_device_ptr(v, "v"))) return rc;
+  if (o && (rc = check_device_ptr(o, "o"))) return rc;
+  return ATTN_OK;
+}
+
+FmhaBf16Args bf16_args(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
+                       const attn_shape* s, float sm_scale) {
+  FmhaBf16Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = s->q_stride[i];
+    a.ks[i] = s->k_stride[i];
+    a.vs[i] = s->v_stride[i];
+    a.os[i] = s->o_stride[i];
+  }
+  a.B = (int)s->B;
+  a.Sq = (int)s->S_q;
+  a.Skv = (int)s->S_kv;
+  a.Hq = (int)s->Hq;
+  a.Hkv = (int)s->Hkv;
+  a.sm_scale = sm_scale;
+  a.o_fp32 = o_dtype == ATTN_DTYPE_FP32;
+  return a;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_recipe(const attn_recipe* r) {
+  if (r == nullptr) return fail(ATTN_ERR_INVALID_ARG, "recipe is NULL");
+  if (r->qk_dtype != ATTN_DTYPE_INT8 && r->qk_dtype != ATTN_DTYPE_FP8_E4M3)
+    return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "qk_dtype must be INT8 or FP8_E4M3");
+  if (r->v_dtype != ATTN_DTYPE_FP8_E4M3) return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "v_dtype must be FP8_E4M3");
+  auto blk_ok = [](int b) { return b == 1 || b == 4 || b == 16; };
+  if (!blk_ok(r->q_block) || !blk_ok(r->k_block))
+    return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "q_block and k_block must be 1, 4 or 16 (got %d, %d)", r->q_block,
+                r->k_block);
+  if (r->v_block != 1) return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "v_block must be 1 (one V scale per channel)");
+  return ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+void sage_layout(const attn_shape* s, const attn_recipe* r, attn_sage_layout* L) {
+  const int64_t S = s->S_q > s->S_kv ? s->S_q : s->S_kv;
+  L->s_pad = (S + kBlockN - 1) / kBlockN * kBlockN;
+  L->n_qblk = (s->S_q + r->q_block - 1) / r->q_block;
+  L->n_kblk = (s->S_kv + r->k_block - 1) / r->k_block;
+  const int64_t nchunks = (s->S_kv + kMeanChunk - 1) / kMeanChunk;
+  size_t off = 0;
+  L->q_codes_off = off;
+  off = align256(off + (size_t)(s->B * s->Hq * L->s_pad * kHeadDim));
+  L->k_codes_off = off;
+  off = align256(off + (size_t)(s->B * s->Hkv * L->s_pad * kHeadDim));
+  L->v_codes_off = off;
+  off = align256(off + (size_t)(s->B * s->Hkv * L->s_pad * kHeadDim));
+  L->q_scale_off = off;
+  off = align256(off + sizeof(float) * (size_t)(s->B * s->Hq * L->n_qblk));
+  L->k_scale_off = off;
+  off = align256(off + sizeof(float) * (size_t)(s->B * s->Hkv * L->n_kblk));
+  L->v_scale_off = off;
+  off = align256(off + sizeof(float) * (size_t)(s->B * s->Hkv * kHeadDim));
+  L->k_mean_off = off;
+  off = align256(off + sizeof(float) * (size_t)(s->B * s->Hkv * kHeadDim));
+  L->scratch_off = off;
+  off = align256(off + sizeof(float) * (size_t)(s->B * s->Hkv * nchunks * kHeadDim));
+  off = align256(off + sizeof(unsigned) * (size_t)(s->B * s->Hkv * kHeadDim));
+  L->total_bytes = off;
+}
+
+int check_sage(const void* q, const void* k, const void* v, const attn_shape* shape, const attn_recipe* recipe,
+               void* ws, size_t ws_bytes, attn_sage_layout* L) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_recipe(recipe))) return rc;
+  sage_layout(shape, recipe, L);
+  if (empty(shape) && shape->S_kv == 0) return ATTN_OK;
+  if (!q || !k || !v) return fail(ATTN_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(ATTN_ERR_BAD_LAYOUT, "q, k, v must be 16-byte aligned");
+  if (ws == nullptr) return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(ATTN_ERR_BAD_LAYOUT, "workspace must be 256-byte aligned");
+  if (ws_bytes < L->total_bytes)
+    return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %zu needed", ws_bytes, L->total_bytes);
+  return ATTN_OK;
+}
+
+SageQuantArgs quant_args(const void* q, const void* k, const void* v, const attn_shape* s, const attn_recipe* r,
+                         void* ws, const attn_sage_layout& L) {
+  SageQuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = s->q_stride[i];
+    a.ks[i] = s->k_stride[i];
+    a.vs[i] = s->v_stride[i];
+  }
+  a.B = (int)s->B;
+  a.Sq = (int)s->S_q;
+  a.Skv = (int)s->S_kv;
+  a.Hq = (int)s->Hq;
+  a.Hkv = (int)s->Hkv;
+  a.qk_int8 = r->qk_dtype == ATTN_DTYPE_INT8;
+  a.q_block = r->q_block;
+  a.k_block = r->k_block;
+  a.s_pad = L.s_pad;
+  a.n_qblk = L.n_qblk;
+  a.n_kblk = L.n_kblk;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  a.q_codes = w + L.q_codes_off;
+  a.k_codes = w + L.k_codes_off;
+  a.v_codes = w + L.v_codes_off;
+  a.q_scale = reinterpret_cast<float*>(w + L.q_scale_off);
+  a.k_scale = reinterpret_cast<float*>(w + L.k_scale_off);
+  a.v_scale = reinterpret_cast<float*>(w + L.v_scale_off);
+  a.k_mean = reinterpret_cast<float*>(w + L.k_mean_off);
+  a.k_partial = reinterpret_cast<float*>(w + L.scratch_off);
+  const int64_t nchunks = (s->S_kv + kMeanChunk - 1) / kMeanChunk;
+  a.v_absmax = reinterpret_cast<unsigned*>(w + align256(L.scratch_off + sizeof(float) * (size_t)(s->B * s->Hkv * nchunks * kHeadDim)));
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return 100; }
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_tile_config(int* block_m, int* block_n) {
+  if (!block_m || !block_n) return fail(ATTN_ERR_INVALID_ARG, "NULL output pointer");
+  *block_m = kWaveRows;
+  *block_n = kBlockN;
+  return ok();
+}
+
+int attn_skip_gate(float t, float disabled_until_timestep, int* enabled) {
+  if (!enabled) return fail(ATTN_ERR_INVALID_ARG, "NULL output pointer");
+  if (!(std::isfinite(t) && t >= 0.0f && t <= 1.0f))
+    return fail(ATTN_ERR_INVALID_ARG, "timestep must be finite and in [0, 1]");
+  if (!(std::isfinite(disabled_until_timestep) && disabled_until_timestep >= 0.0f && disabled_until_timestep <= 1.0f))
+    return fail(ATTN_ERR_INVALID_ARG, "disabled_until_timestep must be finite and in [0, 1]");
+  *enabled = t <= disabled_until_timestep ? 1 : 0;
+  return ok();
+}
+
+int attn_dense_bf16(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
+                    const attn_shape* shape, float sm_scale, void* stream) {
+  int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
+  if (rc) return rc;
+  if (empty(shape)) return ok();
+  if ((rc = check_ptrs(q, k, v, o))) return rc;
+  const FmhaBf16Args a = bf16_args(q, k, v, o, o_dtype, shape, sm_scale);
+  return launched(launch_fmha_bf16(a, false, static_cast<hipStream_t>(stream)), "dense attention");
+}
+
+int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
+                      const attn_shape* shape, float sm_scale, float threshold_factor, uint8_t* skip_bitmap,
+                      uint64_t* skipped_tiles, void* stream) {
+  int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
+  if (rc) return rc;
+  if (!(std::isfinite(threshold_factor) && threshold_factor >= 0.0f))
+    return fail(ATTN_ERR_BAD_THRESHOLD, "threshold factor must be finite and >= 0");
+  if (empty(shape)) return ok();
+  if ((rc = check_ptrs(q, k, v, o))) return rc;
+  if (skip_bitmap && (rc = check_device_ptr(skip_bitmap, "skip_bitmap"))) return rc;
+  if (skipped_tiles) {
+    if ((reinterpret_cast<uintptr_t>(skipped_tiles) & 7u) != 0)
+      return fail(ATTN_ERR_BAD_LAYOUT, "skipped_tiles must be 8-byte aligned");
+    if ((rc = check_device_ptr(skipped_tiles, "skipped_tiles"))) return rc;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FmhaBf16Args a = bf16_args(q, k, v, o, o_dtype, shape, sm_scale);
+  unsigned long long* counter = reinterpret_cast<unsigned long long*>(skipped_tiles);
+  if (counter && (rc = launched(launch_zero_u64(counter, st), "counter reset"))) return rc;
+  if (threshold_factor == 0.0f) {
+    // lambda = 0: nothing can be skipped; run the dense kernel itself.
+    if (skip_bitmap) {
+      const int64_t nqb = (shape->S_q + kWaveRows - 1) / kWaveRows;
+      const int64_t nkt = (shape->S_kv + kBlockN - 1) / kBlockN;
+      const size_t n = (size_t)(shape->B * shape->Hq * nqb * nkt);
+      if ((rc = launched(launch_fill_u8(skip_bitmap, n, 0, st), "bitmap clear"))) return rc;
+    }
+    return launched(launch_fmha_bf16(a, false, st), "dense attention");
+  }
+  a.log2_lambda = (float)std::log2((double)threshold_factor / (double)shape->S_kv);
+  a.bitmap = skip_bitmap;
+  a.counter = counter;
+  return launched(launch_fmha_bf16(a, true, st), "skip-softmax attention");
+}
+
+int attn_sage_layout_query(const attn_shape* shape, const attn_recipe* recipe, attn_sage_layout* out) {
+  if (!out) return fail(ATTN_ERR_INVALID_ARG, "NULL output pointer");
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_recipe(recipe))) return rc;
+  sage_layout(shape, recipe, out);
+  return ok();
+}
+
+int sage_quantize(const void* q, const void* k, const void* v, const attn_shape* shape, const attn_recipe* recipe,
+                  void* ws, size_t ws_bytes, void* stream) {
+  attn_sage_layout L;
+  int rc = check_sage(q, k, v, shape, recipe, ws, ws_bytes, &L);
+  if (rc) return rc;
+  if (shape->B == 0 || (shape->S_q == 0 && shape->S_kv == 0) || shape->Hq == 0) return ok();
+  if ((rc = check_ptrs(q, k, v, nullptr))) return rc;
+  if ((rc = check_device_ptr(ws, "workspace"))) return rc;
+  const SageQuantArgs a = quant_args(q, k, v, shape, recipe, ws, L);
+  return launched(launch_sage_quantize(a, static_cast<hipStream_t>(stream)), "SAGE quantization");
+}
+
+int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype, const attn_shape* shape,
+              const attn_recipe* recipe, float sm_scale, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
+  if (rc) return rc;
+  attn_sage_layout L;
+  if ((rc = check_recipe(recipe))) return rc;
+  if (empty(shape)) return ok();
+  if ((rc = check_sage(q, k, v, shape, recipe, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_ptrs(q, k, v, o))) return rc;
+  if ((rc = check_device_ptr(ws, "workspace"))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SageQuantArgs qa = quant_args(q, k, v, shape, recipe, ws, L);
+  if ((rc = launched(launch_sage_quantize(qa, st), "SAGE quantization"))) return rc;
+  FmhaSageArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_codes = qa.q_codes;
+  a.k_codes = qa.k_codes;
+  a.v_codes = qa.v_codes;
+  a.q_scale = qa.q_scale;
+  a.k_scale = qa.k_scale;
+  a.v_scale = qa.v_scale;
+  a.o = o;
+  for (int i = 0; i < 3; ++i) a.os[i] = shape->o_stride[i];
+  a.B = qa.B;
+  a.Sq = qa.Sq;
+  a.Skv = qa.Skv;
+  a.Hq = qa.Hq;
+  a.Hkv = qa.Hkv;
+  a.s_pad = L.s_pad;
+  a.n_qblk = L.n_qblk;
+  a.n_kblk = L.n_kblk;
+  a.q_block = recipe->q_block;
+  a.k_block = recipe->k_block;
+  a.qk_int8 = qa.qk_int8;
+  a.sm_scale = sm_scale;
+  a.o_fp32 = o_dtype == ATTN_DTYPE_FP32;
+  return launched(launch_fmha_sage(a, st), "SAGE attention");
+}
+
+}  // extern "C"

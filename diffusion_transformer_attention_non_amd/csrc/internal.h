@@ -1,0 +1,76 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ditattn {
+
+// Tile geometry shared by the attention kernels and the host layer.
+constexpr int kHeadDim = 128;
+constexpr int kWaveRows = 64;    // query rows owned by one wavefront (skip decision unit)
+constexpr int kWavesPerWG = 4;
+constexpr int kBlockM = kWaveRows * kWavesPerWG;  // query rows per workgroup
+constexpr int kBlockN = 64;       // keys per KV tile
+constexpr int kMeanChunk = 256;   // tokens per partial sum of the K mean
+
+struct FmhaBf16Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t qs[3], ks[3], vs[3], os[3];  // element strides (b, s, h)
+  int B, Sq, Skv, Hq, Hkv;
+  float sm_scale;
+  int o_fp32;
+  float log2_lambda;                // skip threshold in log2 units (skip kernel only)
+  uint8_t* bitmap;                  // nullable
+  unsigned long long* counter;      // nullable
+};
+
+hipError_t launch_fmha_bf16(const FmhaBf16Args& a, bool skip, hipStream_t stream);
+hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
+hipError_t launch_fill_u8(uint8_t* p, size_t n, uint8_t value, hipStream_t stream);
+
+struct SageQuantArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t qs[3], ks[3], vs[3];
+  int B, Sq, Skv, Hq, Hkv;
+  int qk_int8;          // 1 = int8 codes, 0 = E4M3 codes
+  int q_block, k_block;
+  int64_t s_pad, n_qblk, n_kblk;
+  uint8_t* q_codes;     // [B, Hq, s_pad, 128]
+  uint8_t* k_codes;     // [B, Hkv, s_pad, 128]
+  uint8_t* v_codes;     // [B, Hkv, 128, s_pad]
+  float* q_scale;       // [B, Hq, n_qblk]
+  float* k_scale;       // [B, Hkv, n_kblk]
+  float* v_scale;       // [B, Hkv, 128]
+  float* k_mean;        // [B, Hkv, 128]
+  float* k_partial;     // [B, Hkv, n_chunks, 128]
+  unsigned* v_absmax;   // [B, Hkv, 128] float bits
+};
+
+hipError_t launch_sage_quantize(const SageQuantArgs& a, hipStream_t stream);
+
+struct FmhaSageArgs {
+  const uint8_t* q_codes;
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  void* o;
+  int64_t os[3];
+  int B, Sq, Skv, Hq, Hkv;
+  int64_t s_pad, n_qblk, n_kblk;
+  int q_block, k_block;
+  int qk_int8;
+  float sm_scale;
+  int o_fp32;
+};
+
+hipError_t launch_fmha_sage(const FmhaSageArgs& a, hipStream_t stream);
+
+}  // namespace ditattn

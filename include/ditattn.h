@@ -1,0 +1,192 @@
+/*
+ * ditattn: full-context, non-causal fused multi-head attention for diffusion
+ * transformers on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operations follow these pages (titles as published):
+ *   [TA]  "TRTLLM Attention" (vllm-omni user guide): "Requirements",
+ *         "Dense mode", "Skip-Softmax", "SAGE quantization".
+ *   [DAB] "Diffusion Attention Backends" (vllm-omni user guide): backend
+ *         table ("BF16, GQA native, head_dim=128"), "TRTLLM_ATTN Backend and
+ *         Skip-Softmax", "TRTLLM_ATTN SAGE Quantization".
+ *   [SSD] "SAGE + Skip-Softmax - API Design & Test Plan": Part 1 section 4,
+ *         the knob to kernel-argument table (sage_block_sizes=(q,k,v),
+ *         bmm1_scale/bmm2_scale, threshold = factor / seqlen, the timestep
+ *         gate being host-side with no kernel argument).
+ *   [VQA] "VisualGen Quantized Attention (Beta)": "Recipes" (the recipe tuple
+ *         (qk_dtype, v_dtype, (q_block_size, k_block_size, v_block_size))) and
+ *         "SageAttention in the TRTLLM backend" (one scale per token block per
+ *         head for Q/K; one scale per head per channel for V).
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns an int status: ATTN_OK (0) or a negative attn_status.
+ *     All arguments are validated before anything is launched; an invalid
+ *     call launches nothing and never falls back to another path.
+ *     attn_last_error() gives a message for the calling thread's last failure.
+ *   - Ownership: the caller allocates and owns every buffer.  The library
+ *     never allocates, frees or synchronizes device memory; all work is
+ *     enqueued asynchronously on the caller's stream (`stream`, a
+ *     hipStream_t; NULL = the default stream).  Pointers marked "device" must
+ *     be device memory of the current device, 16-byte aligned.
+ *   - Layout: Q is [B, S_q, Hq, D], K and V are [B, S_kv, Hkv, D], O is
+ *     [B, S_q, Hq, D], each with arbitrary element strides for (b, s, h) given
+ *     in attn_shape and a contiguous d axis.  Strides must be multiples of 8
+ *     elements (16 bytes).  D must be 128 ([TA] "Requirements").  Query head
+ *     h reads KV head h / (Hq / Hkv) ("GQA native", [DAB] backend table).
+ *   - Attention is full-context and non-causal; there is no mask argument
+ *     ([TA] "Requirements": a packed or mask-free path).
+ *   - Calls that run on the same stream are ordered; concurrent calls on
+ *     different streams that share an output buffer or workspace race.
+ */
+#ifndef DITATTN_H
+#define DITATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,          /* null pointer, negative size, bad enum */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = -2, /* D != 128 */
+  ATTN_ERR_BAD_GQA = -3,              /* Hq % Hkv != 0 */
+  ATTN_ERR_UNSUPPORTED_RECIPE = -4,   /* recipe outside the accepted set */
+  ATTN_ERR_BAD_LAYOUT = -5,           /* stride or alignment not supported */
+  ATTN_ERR_BAD_THRESHOLD = -6,        /* factor not finite or negative */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = -7,
+  ATTN_ERR_DEVICE = -8,               /* no device, wrong device, launch failure */
+  ATTN_ERR_NOT_IMPLEMENTED = -9
+} attn_status;
+
+typedef enum {
+  ATTN_DTYPE_BF16 = 0,
+  ATTN_DTYPE_FP32 = 1,
+  ATTN_DTYPE_INT8 = 2,
+  ATTN_DTYPE_FP8_E4M3 = 3             /* OCP OFP8 E4M3 */
+} attn_dtype;
+
+/* Problem shape and strides (in elements).  stride[0..2] = b, s, h. */
+typedef struct {
+  int64_t B, S_q, S_kv, Hq, Hkv, D;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} attn_shape;
+
+/* SAGE recipe ([VQA] "Recipes"): qk_dtype in {INT8, FP8_E4M3}, v_dtype =
+ * FP8_E4M3, q_block and k_block in {1, 4, 16} tokens ([TA], [DAB] key tables),
+ * v_block = 1 (one V scale per head per channel, [VQA]). */
+typedef struct {
+  attn_dtype qk_dtype;
+  attn_dtype v_dtype;
+  int32_t q_block;
+  int32_t k_block;
+  int32_t v_block;
+} attn_recipe;
+
+/* Where sage_quantize puts each quantized tensor inside the workspace (byte
+ * offsets from ws) and how the tensors are laid out:
+ *   q_codes  [B, Hq,  s_pad, 128]  int8 or E4M3 bytes (token rows >= S_q are 0)
+ *   k_codes  [B, Hkv, s_pad, 128]  codes of K - mean (rows >= S_kv are 0)
+ *   v_codes  [B, Hkv, 128, s_pad]  E4M3 bytes, transposed (d-major)
+ *   q_scale  [B, Hq,  n_qblk]      fp32, n_qblk = ceil(S_q / q_block)
+ *   k_scale  [B, Hkv, n_kblk]      fp32, n_kblk = ceil(S_kv / k_block)
+ *   v_scale  [B, Hkv, 128]         fp32
+ *   k_mean   [B, Hkv, 128]         fp32 (the K-smoothing mean)
+ * s_pad is max(S_q, S_kv) rounded up to a multiple of 64. */
+typedef struct {
+  size_t total_bytes;
+  size_t q_codes_off, k_codes_off, v_codes_off;
+  size_t q_scale_off, k_scale_off, v_scale_off, k_mean_off, scratch_off;
+  int64_t s_pad, n_qblk, n_kblk;
+} attn_sage_layout;
+
+/* Dense BF16 attention ([TA] "Dense mode"; [DAB] backend table).
+ *   O = softmax(sm_scale * Q K^T) V, per batch entry and query head.
+ *   q, k, v: device bf16 per the layout above; o: device, o_dtype BF16 or
+ *   FP32 (round to nearest even).  sm_scale: any finite float (typically
+ *   1/sqrt(128)).  Errors: INVALID_ARG, UNSUPPORTED_HEAD_DIM, BAD_GQA,
+ *   BAD_LAYOUT, DEVICE.  Empty problems (B, S_q, Hq = 0) return OK with no
+ *   launch; S_kv = 0 with S_q > 0 is INVALID_ARG (softmax over no keys). */
+int attn_dense_bf16(const void* q, const void* k, const void* v, void* o,
+                    attn_dtype o_dtype, const attn_shape* shape, float sm_scale,
+                    void* stream);
+
+/* Workspace layout for sage_quantize / attn_sage ([VQA] "SageAttention in
+ * the TRTLLM backend").  Host-only; fills *out.  Errors as sage_quantize. */
+int attn_sage_layout_query(const attn_shape* shape, const attn_recipe* recipe,
+                           attn_sage_layout* out);
+
+/* SAGE quantization of Q, K and V into the workspace ([TA] "SAGE
+ * quantization": Q/K per block, V per channel, K-smoothing internal).
+ *   mu[b,g,d] = mean of K over all S_kv tokens (binary32; tokens summed in
+ *     chunks of 256 in ascending order, chunk sums added in ascending order,
+ *     then divided by S_kv);
+ *   K_hat = K - mu; Q and K_hat quantized per block of q_block / k_block
+ *     tokens x 128 channels of one head: a = max|x|, scale = a / QMAX (1 if
+ *     a == 0), code = round_nearest_even(x / scale) saturated to +-QMAX, QMAX
+ *     = 127 (int8) or 448 (E4M3);
+ *   V quantized to E4M3 per (b, kv head, channel) with scale max|v| / 448.
+ * Every division is a correctly rounded binary32 division.  ws must hold
+ * layout.total_bytes (device, 256-byte aligned); the output tensors sit at
+ * the layout's offsets.  Errors: INVALID_ARG, UNSUPPORTED_HEAD_DIM, BAD_GQA,
+ * UNSUPPORTED_RECIPE, BAD_LAYOUT, WORKSPACE_TOO_SMALL, DEVICE. */
+int sage_quantize(const void* q, const void* k, const void* v, const attn_shape* shape,
+                  const attn_recipe* recipe, void* ws, size_t ws_bytes, void* stream);
+
+/* SAGE attention ([TA] "SAGE quantization": both matmuls in low precision;
+ * [SSD] knob table: sage_block_sizes, bmm1_scale / bmm2_scale).
+ *   Runs sage_quantize into ws, then attention on the codes:
+ *   s_ij = sm_scale * sq_i * sk_j * <qc_i, kc_j>; online softmax over KV
+ *   tiles of 64 keys in ascending order; P enters BMM2 as E4M3(2^8 * p) with
+ *   p relative to the running maximum; the row sum takes the unrounded p;
+ *   O = acc * sv_d / (2^8 * l).  o_dtype BF16 or FP32.  Errors as
+ *   sage_quantize. */
+int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
+              const attn_shape* shape, const attn_recipe* recipe, float sm_scale,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Skip-Softmax attention on BF16 ([TA] "Skip-Softmax"; [SSD] knob table:
+ * skip_softmax_threshold_scale_factor, threshold = factor / seqlen).
+ *   lambda = threshold_factor / S_kv.  Queries are tiled in blocks of
+ *   block_m rows and keys in tiles of block_n keys (attn_tile_config).  For
+ *   each query block, KV tiles are visited in ascending order; tile t > 0 is
+ *   skipped when, for every valid row i of the block,
+ *   exp(M_it - m_i) < lambda, where M_it is the row's largest logit in the
+ *   tile and m_i its running maximum over the tiles kept so far.  A skipped
+ *   tile contributes nothing (no exponentials, no P V).  threshold_factor = 0
+ *   runs exactly the dense kernel (bit-identical to attn_dense_bf16).
+ *   skip_bitmap (nullable, device): [B, Hq, ceil(S_q/block_m),
+ *   ceil(S_kv/block_n)] uint8, 1 = skipped.  skipped_tiles (nullable,
+ *   device): receives the number of skipped (query block, KV tile) pairs.
+ *   Errors: as attn_dense_bf16, plus BAD_THRESHOLD (factor not finite or
+ *   < 0). */
+int attn_skip_softmax(const void* q, const void* k, const void* v, void* o,
+                      attn_dtype o_dtype, const attn_shape* shape, float sm_scale,
+                      float threshold_factor, uint8_t* skip_bitmap,
+                      uint64_t* skipped_tiles, void* stream);
+
+/* Host-side timestep gate ([TA] "Skip-Softmax", key disabled_until_timestep;
+ * [SSD]: host-side gate, no kernel argument).  *enabled = (t <= D), with t
+ * the normalized denoising timestep (1 = noisiest, 0 = clean).  Errors:
+ * INVALID_ARG when t or D is not finite or outside [0, 1]. */
+int attn_skip_gate(float t, float disabled_until_timestep, int* enabled);
+
+/* Query and KV tile sizes of the attention kernels (block_m query rows per
+ * skip decision, block_n keys per KV tile).  Host-only. */
+int attn_tile_config(int* block_m, int* block_n);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITATTN_H */

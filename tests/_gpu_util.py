@@ -1,0 +1,36 @@
+"""Helpers shared by the GPU parity tests (comparison metrics, device checks)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+gpu_available = torch.cuda.is_available()
+needs_gpu = pytest.mark.skipif(not gpu_available, reason="needs an MI355X GPU")
+
+
+def announce(msg):
+    """Name the case on stdout before a GPU step, so a failing run says which."""
+    sys.stdout.write(f"[gpu-case] {msg}\n")
+    sys.stdout.flush()
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_l2(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))
+
+
+def dense_tolerances(got, ref):
+    """Dense BF16 parity bar: max-abs <= 1e-2 and rel-L2 <= 5e-3."""
+    ma, rl = max_abs(got, ref), rel_l2(got, ref)
+    assert ma <= 1e-2 and rl <= 5e-3, f"max_abs={ma:.3e} rel_l2={rl:.3e}"
+    return ma, rl

@@ -1,0 +1,92 @@
+"""Dense BF16 attention on the GPU against the oracle's exact attention."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_non_amd as dit
+from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate
+from oracle import exact_attention
+from tests._gpu_util import announce, dense_tolerances, needs_gpu, rel_l2, to_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+SC = 1 / math.sqrt(128)
+
+
+def _run(q, k, v, out_dtype=torch.bfloat16):
+    return dit.attn_dense_bf16(q.cuda(), k.cuda(), v.cuda(), out_dtype=out_dtype)
+
+
+def test_small_config_fp32_out_full_parity():
+    announce("dense B=1 H=2 S=256 fp32 out")
+    q, k, v = generate("dense_b1_h2_s256")
+    o = _run(q, k, v, torch.float32)
+    torch.cuda.synchronize()
+    ref = exact_attention(q, k, v, SC)
+    dense_tolerances(to_np(o), ref)
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv", [
+    (1, 1, 1, 1, 1), (1, 17, 17, 2, 1), (2, 64, 64, 2, 2), (1, 65, 300, 3, 1),
+    (1, 300, 65, 4, 2), (2, 511, 513, 6, 2), (1, 1000, 777, 1, 1), (1, 257, 129, 8, 8)])
+def test_ragged_shapes_and_gqa(B, Sq, Skv, Hq, Hkv):
+    announce(f"dense B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}")
+    q, _, _ = gaussian_qkv(B, Sq, Hq, Hkv, seed=Sq + 7 * Skv)
+    _, k, v = gaussian_qkv(B, Skv, Hq, Hkv, seed=Skv + 3, k_bias_std=2.0)
+    o = _run(q, k, v, torch.float32)
+    torch.cuda.synchronize()
+    dense_tolerances(to_np(o), exact_attention(q, k, v, SC))
+
+
+def test_strided_packed_qkv_layout():
+    announce("dense packed qkv strides")
+    B, S, H = 2, 200, 4
+    qkv = torch.randn(B, S, 3, H, 128, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    d = qkv.cuda()
+    o = dit.attn_dense_bf16(d[:, :, 0], d[:, :, 1], d[:, :, 2], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    dense_tolerances(to_np(o), exact_attention(q, k, v, SC))
+
+
+def test_bf16_output_is_rounded_fp32_output_and_deterministic():
+    announce("dense bf16 vs fp32 output, determinism")
+    q, k, v = gaussian_qkv(1, 700, 2, 2, seed=11)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o32 = dit.attn_dense_bf16(qd, kd, vd, out_dtype=torch.float32)
+    o16 = dit.attn_dense_bf16(qd, kd, vd)
+    o16b = dit.attn_dense_bf16(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(o16, o16b)
+
+
+def test_gqa_full_size_sampled_rows():
+    """B=2, Hq=24, Hkv=8, S=8192 with the per-channel K bias; sampled query rows."""
+    announce("dense GQA B=2 Hq=24 Hkv=8 S=8192")
+    q, k, v = generate("dense_gqa_b2_h24kv8_s8192")
+    o = _run(q, k, v)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 8191], np.random.default_rng(0).integers(0, 8192, 40)]))
+    ref = exact_attention(q, k, v, SC, rows=rows)
+    got = to_np(o)[:, rows]
+    dense_tolerances(got, ref)
+
+
+def test_empty_and_invalid_calls():
+    announce("dense empty / invalid")
+    q, k, v = gaussian_qkv(1, 8, 2, 2, seed=1)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    e = dit.attn_dense_bf16(qd[:, :0], kd, vd)
+    assert e.shape == (1, 0, 2, 128)
+    with pytest.raises(ValueError, match="S_kv"):
+        dit.attn_dense_bf16(qd, kd[:, :0], vd[:, :0])
+    with pytest.raises(ValueError, match="HEAD_DIM"):
+        dit.attn_dense_bf16(qd[..., :64], kd[..., :64], vd[..., :64])
+    with pytest.raises(ValueError, match="GQA"):
+        dit.attn_dense_bf16(torch.cat([qd, qd[:, :, :1]], 2), kd, vd)
+    with pytest.raises(ValueError):
+        dit.attn_dense_bf16(q, k, v)   # host tensors
+    with pytest.raises(ValueError, match="mask"):
+        dit.attention(qd, kd, vd, attn_mask=torch.ones(8, 8, device="cuda"))

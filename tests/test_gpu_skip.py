@@ -1,0 +1,112 @@
+"""Skip-Softmax attention on the GPU against the oracle's skip emulation."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_non_amd as dit
+from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate, positional_qkv
+from oracle import skip_attention
+from tests._gpu_util import announce, needs_gpu, rel_l2, to_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+SC = 1 / math.sqrt(128)
+NORTH_STAR_BAND = 1e-6      # |exp(M - m) - lambda| within this of the threshold is exempt
+
+
+def _log_band(q, k):
+    """fp32 rounding bound on (M - m) * sm_scale: two logits, each a 128-term
+    binary32 dot of exact bf16 products, |error| <= 128 * 2**-24 * sum|q_d k_d|
+    <= 128 * 2**-24 * |q| |k| (Cauchy-Schwarz), plus slack for the scaling."""
+    qn = float(torch.linalg.vector_norm(q.float(), dim=-1).max())
+    kn = float(torch.linalg.vector_norm(k.float(), dim=-1).max())
+    return 2 * 128 * 2.0 ** -24 * SC * qn * kn + 4e-7
+
+
+def _compare_skip_sets(got, ref_skip, ratio, lam, log_band):
+    """Skipped-tile sets must agree except on tiles within the threshold band."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        near = (np.abs(ratio - lam) <= NORTH_STAR_BAND) | (np.abs(np.log(ratio) - math.log(lam)) <= log_band)
+    near &= ~np.isnan(ratio)
+    diff = (got != ref_skip) & ~near
+    assert not diff.any(), f"{int(diff.sum())} tiles differ outside the band (band tiles: {int(near.sum())})"
+    return int(near.sum()), int(((got != ref_skip) & near).sum())
+
+
+def test_factor_zero_is_bit_identical_to_dense():
+    announce("skip factor 0 vs dense")
+    q, k, v = positional_qkv(grid=(2, 8, 24), H=2, seed=1)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    dense = dit.attn_dense_bf16(qd, kd, vd)
+    o, ex = dit.attn_skip_softmax(qd, kd, vd, 0.0, return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, dense)
+    assert int(ex["bitmap"].sum()) == 0 and int(ex["skipped"][0]) == 0
+
+
+@pytest.mark.parametrize("grid,H,factor", [((2, 8, 24), 2, 1.0), ((2, 8, 24), 2, 10.0), ((2, 8, 24), 2, 100.0),
+                                           ((3, 9, 17), 3, 30.0), ((1, 1, 200), 2, 50.0)])
+def test_skip_set_and_output_match_oracle(grid, H, factor):
+    announce(f"skip grid={grid} H={H} factor={factor}")
+    bm, bn = dit.tile_config()
+    q, k, v = positional_qkv(grid=grid, H=H, seed=2)
+    S = q.shape[1]
+    o, ex = dit.attn_skip_softmax(q.cuda(), k.cuda(), v.cuda(), factor, out_dtype=torch.float32,
+                                  return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    ref, skipped, ratio, rows = skip_attention(q, k, v, SC, factor, bm, bn)
+    got = ex["bitmap"].cpu().numpy().astype(bool)
+    assert got.shape == skipped.shape
+    band, flips = _compare_skip_sets(got, skipped, ratio, factor / S, _log_band(q, k))
+    assert int(ex["skipped"][0]) == int(got.sum())
+    assert not got[..., 0].any()
+    r = rel_l2(to_np(o)[:, rows], ref)
+    assert r <= 3e-2, r
+    if flips == 0:
+        assert r <= 5e-3, r
+
+
+def test_gaussian_inputs_rarely_skip_and_stay_exact():
+    announce("skip gaussian inputs")
+    q, k, v = gaussian_qkv(1, 1000, 2, 1, seed=9)
+    o, ex = dit.attn_skip_softmax(q.cuda(), k.cuda(), v.cuda(), 1.0, return_bitmap=True)
+    torch.cuda.synchronize()
+    bm, bn = dit.tile_config()
+    ref, skipped, ratio, rows = skip_attention(q, k, v, SC, 1.0, bm, bn)
+    _compare_skip_sets(ex["bitmap"].cpu().numpy().astype(bool), skipped, ratio, 1.0 / 1000, _log_band(q, k))
+    assert rel_l2(to_np(o), ref) <= 5e-3
+
+
+def test_invalid_threshold_rejected():
+    q, k, v = gaussian_qkv(1, 8, 1, 1, seed=0)
+    for bad in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(ValueError, match="THRESHOLD"):
+            dit.attn_skip_softmax(q.cuda(), k.cuda(), v.cuda(), bad)
+
+
+def test_wan_shape_sampled_tiles():
+    """B=1, H=40, S=75,600 (21 x 45 x 80 grid), spatially peaked Q/K; sampled query tiles."""
+    announce("skip wan S=75600 H=40 generate")
+    q, k, v = generate("skip_wan_b1_h40_s75600")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    bm, bn = dit.tile_config()
+    S = q.shape[1]
+    nqt = -(-S // bm)
+    heads = [0, 21, 39]
+    qtiles = np.array([0, 517, nqt - 1])
+    band = _log_band(q, k)
+    for factor in (1.0, 10.0, 100.0):
+        announce(f"skip wan factor={factor}")
+        o, ex = dit.attn_skip_softmax(qd, kd, vd, factor, return_bitmap=True, return_count=True)
+        torch.cuda.synchronize()
+        bitmap = ex["bitmap"].cpu().numpy().astype(bool)
+        frac = bitmap.mean()
+        assert int(ex["skipped"][0]) == int(bitmap.sum())
+        for h in heads:
+            ref, skipped, ratio, rows = skip_attention(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], SC,
+                                                       factor, bm, bn, qtiles=qtiles)
+            _compare_skip_sets(bitmap[:, h:h + 1, qtiles], skipped, ratio, factor / S, band)
+            r = rel_l2(to_np(o[:, rows, h:h + 1]), ref)
+            assert r <= 3e-2, (factor, h, r)
+        print(f"factor {factor}: skipped fraction {frac:.4f}")
