@@ -2,17 +2,21 @@
 
 This module only draws random tensors and lays them out; it holds none of the
 attention method's arithmetic, so both the CPU oracle's tests and the HIP
-path's tests and benchmark can take their inputs from it.
+path's tests and benchmark take their inputs from it.
 
-Every tensor is drawn in float32 from ``numpy.random.Generator(PCG64(seed))``
-in a fixed order and rounded to bfloat16 (round-to-nearest-even, by torch's
-conversion).  Layout is ``[B, S, H, D]`` with ``D`` contiguous, as the
-"packed, mask-free" layout of the TRTLLM Attention page (section
-"Requirements") describes.
+Random draws come from torch's counter-based generator (Philox on a GPU,
+torch's CPU generator on the host) seeded with ``seed``, in float32, in a
+fixed order, then rounded to bfloat16 (round-to-nearest-even, torch's
+conversion).  The same seed, shape and device give the same tensors on every
+run; a test generates once and hands the very same tensor to the HIP path and
+to the oracle.  Large inputs are drawn on the GPU (``device="cuda"``) so that
+Wan-sized tensors take seconds, not minutes.
 
-Workloads (``WORKLOADS``) mirror the shapes the pages run on: Wan 2.2 video
-(token grid 21 x 45 x 80 = 75,600, 40 heads, head_dim 128), plus a GQA and a
-small case.  No dataset, prompt or checkpoint is involved.
+Layout is ``[B, S, H, D]`` with ``D`` contiguous, the packed, mask-free layout
+of the "TRTLLM Attention" page (section "Requirements").  Workloads
+(``WORKLOADS``) mirror the shapes the pages run on: Wan 2.2 video (token grid
+21 x 45 x 80 = 75,600, 40 heads, head_dim 128), a GQA case and a small case.
+No dataset, prompt or checkpoint is involved.
 """
 from __future__ import annotations
 
@@ -58,35 +62,42 @@ WORKLOADS = {
 }
 
 
-def _rng(seed: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(seed))
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
 
 
-def _to_bf16(x: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+def _randn(shape, g, device, std=1.0):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x
 
 
 def gaussian_qkv(B, S, Hq, Hkv, D=HEAD_DIM, seed=0, k_bias_std=0.0, outliers=0,
-                 outlier_mult=8.0, std=1.0):
-    """Q, V ~ N(0, std); K ~ N(0, std) + bias[h, d].
+                 outlier_mult=8.0, std=1.0, device="cpu"):
+    """Q, V ~ N(0, std); K ~ N(0, std) + bias[h, d]; bfloat16 [B, S, H, D].
 
     The bias is one value per (KV head, channel), shared by every token and
     batch entry, drawn N(0, k_bias_std) (second argument = standard
     deviation).  ``outliers`` channel indices, the same for every head, get
-    their bias multiplied by ``outlier_mult``.  Draw order: Q, K, V, bias,
-    outlier indices.
+    their bias multiplied by ``outlier_mult``.  Draw order on the device
+    generator: Q, K, V; the bias and the outlier indices come from a host
+    generator seeded with seed + 1.
     """
-    rng = _rng(seed)
-    q = _to_bf16(rng.standard_normal((B, S, Hq, D), dtype=np.float32) * np.float32(std))
-    kf = rng.standard_normal((B, S, Hkv, D), dtype=np.float32) * np.float32(std)
-    v = _to_bf16(rng.standard_normal((B, S, Hkv, D), dtype=np.float32) * np.float32(std))
+    g = _gen(seed, device)
+    q = _randn((B, S, Hq, D), g, device, std).to(torch.bfloat16)
+    kf = _randn((B, S, Hkv, D), g, device, std)
+    v = _randn((B, S, Hkv, D), g, device, std).to(torch.bfloat16)
     if k_bias_std > 0.0:
-        bias = rng.standard_normal((Hkv, D), dtype=np.float32) * np.float32(k_bias_std)
+        rng = np.random.Generator(np.random.PCG64(seed + 1))
+        bias = rng.standard_normal((Hkv, D)).astype(np.float32) * np.float32(k_bias_std)
         if outliers:
             idx = rng.choice(D, size=outliers, replace=False)
             bias[:, idx] *= np.float32(outlier_mult)
-        kf += bias[None, None, :, :]
-    k = _to_bf16(kf)
+        kf += torch.from_numpy(bias).to(kf.device)[None, None]
+    k = kf.to(torch.bfloat16)
     del kf
     return q, k, v
 
@@ -114,41 +125,49 @@ def position_code(grid, D=HEAD_DIM):
     return np.stack(cols, axis=1)
 
 
-def positional_qkv(grid=WAN_GRID, H=40, D=HEAD_DIM, seed=0, noise=0.5, alpha=1.456, B=1):
-    """Spatially peaked Q/K: 0.5 * N(0,1) + alpha * R_h c(n); V ~ N(0,1).
+def head_rotations(H, D=HEAD_DIM, seed=0):
+    """Per-head orthogonal matrices: QR of a Gaussian matrix, signs fixed by R's diagonal."""
+    rng = np.random.Generator(np.random.PCG64(seed + 2))
+    out = np.empty((H, D, D))
+    for h in range(H):
+        qm, rm = np.linalg.qr(rng.standard_normal((D, D)))
+        out[h] = qm * np.sign(np.diag(rm))[None, :]
+    return out
 
-    c(n) is ``position_code``; R_h is a per-head orthogonal matrix (QR of a
-    Gaussian matrix with the signs of R's diagonal folded in), the stand-in
-    for the learned projection.  With alpha = 1.456 the self logit sits about
-    12 above the far field at scale 1/sqrt(128).  Draw order: Q noise, K
-    noise, V, then the H Gaussian matrices.
+
+def positional_qkv(grid=WAN_GRID, H=40, D=HEAD_DIM, seed=0, noise=0.5, alpha=1.456, B=1, device="cpu"):
+    """Spatially peaked Q/K: noise * N(0,1) + alpha * R_h c(n); V ~ N(0,1).
+
+    c(n) is ``position_code``; R_h (``head_rotations``) is the per-head
+    stand-in for the learned projection.  With alpha = 1.456 the self logit
+    sits about 12 above the far field at scale 1/sqrt(128).  Draw order on the
+    device generator: Q noise, K noise, V; the projection is added in float64
+    and the sum rounded to float32, then to bfloat16.
     """
     S = grid[0] * grid[1] * grid[2]
-    rng = _rng(seed)
-    qn = rng.standard_normal((B, S, H, D), dtype=np.float32) * np.float32(noise)
-    kn = rng.standard_normal((B, S, H, D), dtype=np.float32) * np.float32(noise)
-    v = _to_bf16(rng.standard_normal((B, S, H, D), dtype=np.float32))
-    code = position_code(grid, D)
+    g = _gen(seed, device)
+    qn = _randn((B, S, H, D), g, device, noise)
+    kn = _randn((B, S, H, D), g, device, noise)
+    v = _randn((B, S, H, D), g, device).to(torch.bfloat16)
+    code = torch.from_numpy(position_code(grid, D)).to(device)
+    rot = torch.from_numpy(head_rotations(H, D, seed)).to(device)
     for h in range(H):
-        g = rng.standard_normal((D, D))
-        qm, rm = np.linalg.qr(g)
-        qm = qm * np.sign(np.diag(rm))[None, :]
-        proj = (alpha * (code @ qm.T)).astype(np.float32)
+        proj = (alpha * (code @ rot[h].T)).to(torch.float32)
         qn[:, :, h, :] += proj[None]
         kn[:, :, h, :] += proj[None]
-    q = _to_bf16(qn)
+    q = qn.to(torch.bfloat16)
     del qn
-    k = _to_bf16(kn)
+    k = kn.to(torch.bfloat16)
     del kn
     return q, k, v
 
 
-def generate(name: str, seed: int = 0, S: int | None = None, H: int | None = None):
+def generate(name: str, seed: int = 0, S: int | None = None, H: int | None = None, device="cpu"):
     """Inputs of a named workload, optionally with fewer tokens or heads.
 
     A smaller ``S`` keeps the value distribution of the workload (for the
     positional generator the grid is cut to whole frames when it can be, else
-    to a 1 x 1 x S line).  Returns (q, k, v) as CPU bfloat16 tensors.
+    to a 1 x 1 x S line).  Returns (q, k, v) bfloat16 tensors on ``device``.
     """
     w = WORKLOADS[name]
     S = w.S if S is None else S
@@ -156,12 +175,12 @@ def generate(name: str, seed: int = 0, S: int | None = None, H: int | None = Non
     Hkv = w.Hkv if H is None else max(1, H * w.Hkv // w.Hq)
     if w.gen == "gauss":
         return gaussian_qkv(w.B, S, Hq, Hkv, seed=seed, k_bias_std=w.k_bias_std,
-                            outliers=w.outliers)
+                            outliers=w.outliers, device=device)
     grid = w.grid
     if S != grid[0] * grid[1] * grid[2]:
         per_frame = grid[1] * grid[2]
         grid = (S // per_frame, grid[1], grid[2]) if S % per_frame == 0 else (1, 1, S)
-    return positional_qkv(grid, H=Hq, seed=seed, B=w.B)
+    return positional_qkv(grid, H=Hq, seed=seed, B=w.B, device=device)
 
 
 def attention_flops(B, S_q, S_kv, Hq, D=HEAD_DIM):

@@ -65,8 +65,9 @@ def test_bf16_output_is_rounded_fp32_output_and_deterministic():
 def test_gqa_full_size_sampled_rows():
     """B=2, Hq=24, Hkv=8, S=8192 with the per-channel K bias; sampled query rows."""
     announce("dense GQA B=2 Hq=24 Hkv=8 S=8192")
-    q, k, v = generate("dense_gqa_b2_h24kv8_s8192")
-    o = _run(q, k, v)
+    qd, kd, vd = generate("dense_gqa_b2_h24kv8_s8192", device="cuda")
+    q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
+    o = dit.attn_dense_bf16(qd, kd, vd)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, 1, 255, 256, 8191], np.random.default_rng(0).integers(0, 8192, 40)]))
     ref = exact_attention(q, k, v, SC, rows=rows)

@@ -66,9 +66,9 @@ def test_full_size_sampled(name):
     w = WORKLOADS[name]
     dt, _, (qb, kb, _) = w.recipe
     announce(f"{name} generate")
-    q, k, v = generate(name)
+    qd, kd, vd = generate(name, device="cuda")
+    q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
     rec = dit.SageRecipe(dt, "fp8", qb, kb, 1)
-    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     announce(f"{name} sage_quantize")
     gpu = dit.sage_quantize(qd, kd, vd, rec)
     torch.cuda.synchronize()

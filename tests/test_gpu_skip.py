@@ -88,8 +88,8 @@ def test_invalid_threshold_rejected():
 def test_wan_shape_sampled_tiles():
     """B=1, H=40, S=75,600 (21 x 45 x 80 grid), spatially peaked Q/K; sampled query tiles."""
     announce("skip wan S=75600 H=40 generate")
-    q, k, v = generate("skip_wan_b1_h40_s75600")
-    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    qd, kd, vd = generate("skip_wan_b1_h40_s75600", device="cuda")
+    q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
     bm, bn = dit.tile_config()
     S = q.shape[1]
     nqt = -(-S // bm)
