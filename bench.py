@@ -122,7 +122,8 @@ def cpu_baseline(budget_s, S, H, step_flops):
     t0 = time.perf_counter()
     quant = sage_quantize(q4, k4, v4, "fp8", 1, 4)
     t_quant = time.perf_counter() - t0
-    t_sage, n_sage = per_tile(lambda t: sage_attention(quant, sc, bn, rows=np.arange(t * bm, min(S, t * bm + bm))))
+    kv = dit.kv_tile()
+    t_sage, n_sage = per_tile(lambda t: sage_attention(quant, sc, kv, rows=np.arange(t * bm, min(S, t * bm + bm))))
     step_s = (t_dense + t_skip + t_sage) * nqt * H + t_quant * H
     blas = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas")
     return {
@@ -205,7 +206,8 @@ def main():
                 for i, (name, _) in enumerate(calls)}
 
     F = eff_flops(B, S, H, D)
-    nqb, nkt = -(-S // 64), -(-S // 64)
+    vote_m, vote_n = dit.tile_config()
+    nqb, nkt = -(-S // vote_m), -(-S // vote_n)
     skip_frac = float(skipped[0][0]) / (B * H * nqb * nkt) if skipped[0] is not None else 0.0
     step_flops = F * len(calls)
     modes = {

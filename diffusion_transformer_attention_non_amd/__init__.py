@@ -92,7 +92,7 @@ def _lib():
             "attn_sage": [P, P, P, P, I, SP, RP, F, P, ctypes.c_size_t, P],
             "attn_skip_softmax": [P, P, P, P, I, SP, F, F, P, P, P],
             "attn_skip_gate": [F, F, ctypes.POINTER(I)],
-            "attn_tile_config": [ctypes.POINTER(I), ctypes.POINTER(I)],
+            "attn_tile_config": [ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
             "attn_version": [],
         }
         for name, args in sig.items():
@@ -116,10 +116,17 @@ def _check(rc: int):
 
 
 def tile_config():
-    """(block_m, block_n): query rows per skip decision and keys per KV tile."""
-    bm, bn = ctypes.c_int(), ctypes.c_int()
-    _check(_lib().attn_tile_config(ctypes.byref(bm), ctypes.byref(bn)))
+    """(block_m, block_n): query rows and keys per Skip-Softmax vote."""
+    bm, bn, kv = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib().attn_tile_config(ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(kv)))
     return bm.value, bn.value
+
+
+def kv_tile():
+    """Keys per KV tile of the online softmax (SAGE's P rounding follows it)."""
+    bm, bn, kv = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib().attn_tile_config(ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(kv)))
+    return kv.value
 
 
 def _stream(t: torch.Tensor):

@@ -33,9 +33,17 @@ def hipcc():
     return path
 
 
+# Per-source extra flags.  The attention kernels keep their MFMA accumulators
+# in VGPRs (the softmax reads them directly); the default heuristic moves
+# them to AGPRs and copies them back every tile.
+EXTRA_FLAGS = {
+    "fmha_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str, obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -95,6 +95,15 @@ int check_shape(const attn_shape* s) {
 
 bool empty(const attn_shape* s) { return s->B == 0 || s->S_q == 0 || s->Hq == 0; }
 
+// The BF16 kernels address one (batch, kv head)'s K and V rows through 32-bit
+// buffer offsets, including up to four tiles past the end.
+int check_kv_span(const attn_shape* s) {
+  const int64_t rows = s->S_kv + 4 * kBlockN;
+  if (rows * s->k_stride[1] * 2 >= ((int64_t)1 << 32) || rows * s->v_stride[1] * 2 >= ((int64_t)1 << 32))
+    return fail(ATTN_ERR_INVALID_ARG, "K/V span of one head exceeds 4 GiB");
+  return ATTN_OK;
+}
+
 int check_common(const void* q, const void* k, const void* v, const void* o, attn_dtype o_dtype,
                  const attn_shape* shape, float sm_scale) {
   int rc = check_shape(shape);
@@ -253,10 +262,11 @@ int attn_version(void) { return 100; }
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_tile_config(int* block_m, int* block_n) {
-  if (!block_m || !block_n) return fail(ATTN_ERR_INVALID_ARG, "NULL output pointer");
+int attn_tile_config(int* block_m, int* block_n, int* kv_tile) {
+  if (!block_m || !block_n || !kv_tile) return fail(ATTN_ERR_INVALID_ARG, "NULL output pointer");
   *block_m = kWaveRows;
-  *block_n = kBlockN;
+  *block_n = kSkipBlockN;
+  *kv_tile = kBlockN;
   return ok();
 }
 
@@ -275,6 +285,7 @@ int attn_dense_bf16(const void* q, const void* k, const void* v, void* o, attn_d
   int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
   if (rc) return rc;
   if (empty(shape)) return ok();
+  if ((rc = check_kv_span(shape))) return rc;
   if ((rc = check_ptrs(q, k, v, o))) return rc;
   const FmhaBf16Args a = bf16_args(q, k, v, o, o_dtype, shape, sm_scale);
   return launched(launch_fmha_bf16(a, false, static_cast<hipStream_t>(stream)), "dense attention");
@@ -288,6 +299,7 @@ int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn
   if (!(std::isfinite(threshold_factor) && threshold_factor >= 0.0f))
     return fail(ATTN_ERR_BAD_THRESHOLD, "threshold factor must be finite and >= 0");
   if (empty(shape)) return ok();
+  if ((rc = check_kv_span(shape))) return rc;
   if ((rc = check_ptrs(q, k, v, o))) return rc;
   if (skip_bitmap && (rc = check_device_ptr(skip_bitmap, "skip_bitmap"))) return rc;
   if (skipped_tiles) {
@@ -303,7 +315,7 @@ int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn
     // lambda = 0: nothing can be skipped; run the dense kernel itself.
     if (skip_bitmap) {
       const int64_t nqb = (shape->S_q + kWaveRows - 1) / kWaveRows;
-      const int64_t nkt = (shape->S_kv + kBlockN - 1) / kBlockN;
+      const int64_t nkt = (shape->S_kv + kSkipBlockN - 1) / kSkipBlockN;
       const size_t n = (size_t)(shape->B * shape->Hq * nqb * nkt);
       if ((rc = launched(launch_fill_u8(skip_bitmap, n, 0, st), "bitmap clear"))) return rc;
     }

@@ -20,16 +20,32 @@
 //   Computing the transposed products keeps each query in one lane, so the
 //   softmax state (max, sum, rescale factor) never leaves the lane.
 //
+// Pipeline
+//   K/V tiles stream into a 4-stage LDS ring with buffer_load ... lds (no
+//   register staging; out-of-range rows read as zero), three tiles ahead; the
+//   loop is unrolled by the ring depth so every stage is a distinct array.
+//   The dense kernel splits each tile into two 32-key halves and runs four
+//   blocks per tile, each pairing MFMA work with independent VALU work:
+//     A: BMM1 (j, half 1)    || exponentials (j, half 0)
+//     B: BMM2 (j, half 0)    || row max (j, half 1), row sums (j, half 0)
+//     C: BMM1 (j+1, half 0)  || exponentials (j, half 1)
+//     D: BMM2 (j, half 1)    || row max (j+1, half 0), row sums (j, half 1)
+//   The order inside a block is written out (MFMA, its share of VALU work,
+//   scheduling fence), with LDS fragments read two MFMA steps ahead.
+//
 // Online softmax with a lazy reference maximum: exponentials are taken
 // relative to a per-row reference m_ref (log2 units) that is raised only when
 // a tile's maximum exceeds it by more than 8, so P <= 2^8 and the O rescale
 // runs only when some row's maximum grows that much.  Softmax is invariant to
 // the reference, so the result is the same up to rounding.
 //
-// Skip-Softmax (kSkip): after BMM1 of tile t > 0, the wavefront skips the tile
-// (no exponentials, no BMM2) when every valid row i of its 64 rows has
-// exp(M_it - m_i) < lambda, M_it being the row's tile maximum and m_i the
-// running maximum over the tiles kept so far; lambda = factor / S_kv.
+// Skip-Softmax (kSkip): the KV tile of the vote is a 32-key half.  After its
+// BMM1, the wavefront skips the half (no exponentials, no BMM2) when every
+// valid row i of its 64 rows has exp(M_it - m_i) < lambda, M_it being the
+// row's maximum over the half and m_i the running maximum over the halves
+// kept so far; lambda = factor / S_kv.  The first half is always kept.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -39,34 +55,70 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the reference max moves
+constexpr int kRowBytes = kHeadDim * 2;                 // one bf16 row of 128 channels
+constexpr int kTileBytes = kBlockN * kRowBytes;         // 16 KB per K or V tile
+constexpr int kLoadsPerTile = 8;                        // buffer->LDS loads per wavefront per tile
+constexpr int kBufferFlags = 0x00020000;                // raw buffer, 32-bit data format
 
-// LDS layout of one pipeline stage (bf16 elements):
-//   K tile: 64 rows x 128 (+8 pad), rows stored in MFMA-row order (see
-//           kv_row_of_key), 272-byte stride: the 8 lanes of a ds_read_b128
-//           phase read 8 consecutive rows and land in 8 distinct 16-byte banks.
-//   V tile: 64 keys x 128 (+16 pad) row-major, 288-byte stride: the 16 lanes
-//           of a ds_read_b64_tr_b16 phase read 4 rows x 32 bytes that cover
-//           the 128 bank bytes exactly once.
-constexpr int kKRow = 136;
-constexpr int kVRow = 144;
-constexpr int kKTile = kBlockN * kKRow;
-constexpr int kVTile = kBlockN * kVRow;
-constexpr int kStage = kKTile + kVTile;
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// sched_group_barrier instruction classes.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// bf16 pair jp (0..3) of an 8-element vector.  Written as constant shuffles:
+// extracting a lane of the bit-cast int vector instead was lowered to lane 0
+// for every jp by the compiler used here.
+__device__ __forceinline__ bf16x2 bf16_pair(const bf16x8 v, int jp) {
+  switch (jp) {
+    case 0: return __builtin_shufflevector(v, v, 0, 1);
+    case 1: return __builtin_shufflevector(v, v, 2, 3);
+    case 2: return __builtin_shufflevector(v, v, 4, 5);
+    default: return __builtin_shufflevector(v, v, 6, 7);
+  }
+}
 
 // Accumulator register r of lane half h in a 32x32 S^T block holds MFMA row
-// 8*(r/4) + 4*h + r%4.  Reading K row "key(i)" for MFMA row i with
+// 8*(r/4) + 4*h + r%4.  Feeding MFMA row i with key
 //   key(8a + 4h + b) = 16*(a/2) + 8*h + 4*(a%2) + b
-// makes register r of lane half h hold key 16*(r/8) + 8*h + r%8, i.e. each
-// lane half holds runs of 8 consecutive keys: exactly the B-operand slots of
-// the BMM2 MFMA (8 consecutive k per lane half).  This maps a key to its row.
-__device__ __forceinline__ int kv_row_of_key(int k) {
-  const int a = 2 * (k >> 4) + ((k >> 2) & 1);
-  return 8 * a + 4 * ((k >> 3) & 1) + (k & 3);
+// makes register r of lane half h hold key 16*(r/8) + 8*h + r%8: each lane
+// half holds runs of 8 consecutive keys, exactly the B-operand slots of the
+// BMM2 MFMA (8 consecutive k per lane half).
+__device__ __forceinline__ int key_of_mfma_row(int i) {
+  const int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
+  return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
+
+// LDS tile layouts (16-byte chunks, 16 per 256-byte row, XOR-swizzled so that
+// every read phase hits distinct banks and every read address is a lane
+// constant plus an immediate):
+//   K: row r = MFMA row (32*(r/32) + key_of_mfma_row(r%32) is the key),
+//      physical chunk = logical chunk ^ (r & 7);
+//   V: row = key, physical chunk = logical chunk ^ (2 * (key & 3)).
 
 template <bool kSkip>
 __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK3[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV3[kTileBytes];
+  auto kst = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return sK0; else if constexpr (S == 1) return sK1;
+    else if constexpr (S == 2) return sK2; else return sK3;
+  };
+  auto vst = [&](auto s) -> uint8_t* {
+    constexpr int S = decltype(s)::value;
+    if constexpr (S == 0) return sV0; else if constexpr (S == 1) return sV1;
+    else if constexpr (S == 2) return sV2; else return sV3;
+  };
 
   const int nqt = (p.Sq + kBlockM - 1) / kBlockM;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -80,8 +132,9 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int q0 = qt * kBlockM + wave * kWaveRows;
   const int Sq = p.Sq, Skv = p.Skv;
+  const int nkt = (Skv + kBlockN - 1) / kBlockN;
 
-  // Q fragments, B operand of BMM1: lane (query l32 of block qb, half hh)
+  // ---- Q fragments, B operand of BMM1: lane (query l32 of block qb, half hh)
   // holds d = 16*ds + 8*hh + 0..7.
   bf16x8 qf[2][8];
 #pragma unroll
@@ -97,42 +150,52 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     }
   }
 
-  // Global -> LDS loader: thread covers rows 16*i + tid/16 (i = 0..3) of the
-  // tile, 16-byte chunk tid % 16.
-  const bf16_t* kg = static_cast<const bf16_t*>(p.k) + b * p.ks[0] + g * p.ks[2];
-  const bf16_t* vg = static_cast<const bf16_t*>(p.v) + b * p.vs[0] + g * p.vs[2];
-  const int lrow = tid >> 4, lchunk = tid & 15;
-  int k_dst[4], v_dst[4];
+  // ---- Buffer resources over this (b, kv head)'s K and V rows; rows past
+  // S_kv are out of range and load as zero.
+  const uint32_t kstride = (uint32_t)(p.ks[1] * 2), vstride = (uint32_t)(p.vs[1] * 2);
+  const char* kbase = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.k) + b * p.ks[0] + g * p.ks[2]);
+  const char* vbase = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.v) + b * p.vs[0] + g * p.vs[2]);
+  const __amdgpu_buffer_rsrc_t krsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)(kstride * (uint32_t)Skv), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)(vstride * (uint32_t)Skv), kBufferFlags);
+
+  // Load slots: round i (0..3) of the workgroup covers LDS bytes [4096 i, 4096 i + 4096);
+  // lane fills 16-byte slot 256 i + 64 wave + lane = row 16 i + 4 wave + lane/16, chunk lane%16.
+  uint32_t koff[4], voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 16 * i + lrow;
-    k_dst[i] = (32 * (r >> 5) + kv_row_of_key(r & 31)) * kKRow + 8 * lchunk;
-    v_dst[i] = kKTile + r * kVRow + 8 * lchunk;
+    const int r = 16 * i + 4 * wave + (lane >> 4);
+    const int pch = lane & 15;
+    const int kkey = 32 * (r >> 5) + key_of_mfma_row(r & 31);
+    koff[i] = (uint32_t)kkey * kstride + 16u * (uint32_t)(pch ^ (r & 7));
+    voff[i] = (uint32_t)r * vstride + 16u * (uint32_t)(pch ^ (2 * (r & 3)));
   }
-  uint4 kreg[4], vreg[4];
-  auto gload = [&](int t) {
+  auto issue_loads = [&](auto s, int t) {
+    const uint32_t tk = (uint32_t)t * kBlockN * kstride, tv = (uint32_t)t * kBlockN * vstride;
+    uint8_t* kd = kst(s) + 1024 * wave;
+    uint8_t* vd = vst(s) + 1024 * wave;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = t * kBlockN + 16 * i + lrow;
-      const bool ok = key < Skv;
-      const int64_t kk = ok ? key : 0;
-      kreg[i] = ok ? ldg16(kg + kk * p.ks[1] + 8 * lchunk) : make_uint4(0, 0, 0, 0);
-      vreg[i] = ok ? ldg16(vg + kk * p.vs[1] + 8 * lchunk) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int stage) {
-    bf16_t* base = smem + stage * kStage;
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (DITATTN_LDS void*)(kd + 4096 * i), 16, koff[i] + tk, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(base + k_dst[i]) = kreg[i];
-      *reinterpret_cast<uint4*>(base + v_dst[i]) = vreg[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (DITATTN_LDS void*)(vd + 4096 * i), 16, voff[i] + tv, 0, 0, 0);
   };
 
-  // Lane-dependent parts of the LDS read addresses.
-  const int ka_lane = l32 * kKRow + 8 * hh;
-  const int r16 = lane & 15;
-  const int va_lane = kKTile + (8 * hh + (r16 >> 2)) * kVRow + 16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
+  // ---- LDS read addresses (lane constants; the rest is immediate).
+  int ka[4], va[2];
+  {
+    const int f = l32 & 7;
+#pragma unroll
+    for (int dl = 0; dl < 4; ++dl) ka[dl] = l32 * kRowBytes + 16 * (hh ^ (f & 1)) + 32 * (dl ^ (f >> 1));
+    const int r16 = lane & 15, gq = lane >> 4;
+    const int x = 2 * (gq & 1) + ((r16 & 3) >> 1);
+    const int y = 2 * (r16 >> 2);
+#pragma unroll
+    for (int dl = 0; dl < 2; ++dl)
+      va[dl] = (8 * hh + (r16 >> 2)) * kRowBytes + 64 * (dl ^ (y >> 2)) + 16 * (x ^ (y & 3)) + 8 * (r16 & 1);
+  }
 
   f32x16 o[4][2];
 #pragma unroll
@@ -143,145 +206,324 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
       for (int r = 0; r < 16; ++r) o[db][qb][r] = 0.0f;
 
   const float c = p.sm_scale * kLog2e;
-  float mref[2] = {kNegInf, kNegInf};
-  float mrun[2] = {kNegInf, kNegInf};
+  float mref[2], mrun[2];
   float lsum[2] = {0.0f, 0.0f};
   const bool qvalid0 = q0 + l32 < Sq, qvalid1 = q0 + 32 + l32 < Sq;
   unsigned skipped = 0;
-  const int nkt = (Skv + kBlockN - 1) / kBlockN;
   const int nqb = (Sq + kWaveRows - 1) / kWaveRows;
+  const int nvote = (Skv + kSkipBlockN - 1) / kSkipBlockN;
   uint8_t* bitmap_row = nullptr;
   if (kSkip && p.bitmap != nullptr && q0 < Sq)
-    bitmap_row = p.bitmap + ((int64_t)(b * p.Hq + h) * nqb + q0 / kWaveRows) * nkt;
+    bitmap_row = p.bitmap + ((int64_t)(b * p.Hq + h) * nqb + q0 / kWaveRows) * nvote;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  f32x16 s0[2], s1[2];   // S^T of the tile's two 32-key halves, [qb]
+  bf16x8 pf[2][2][2];    // P^T of the tile, [half][16-key step][qb]
 
-  for (int t = 0; t < nkt; ++t) {
-    const bf16_t* st = smem + (t & 1) * kStage;
-    if (t + 1 < nkt) gload(t + 1);
-
-    // ---- BMM1: S^T = K Q^T over d = 128 (8 steps of 16).
-    f32x16 s[2][2];
+  // BMM1 of one 32-key half from K stage ks (16 MFMAs, 8 LDS reads).
+  auto bmm1 = [&](const uint8_t* ks, int kb, f32x16 (&s)[2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) s[qb][r] = 0.0f;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ka[ds & 3] + kb * 32 * kRowBytes + 128 * (ds >> 2));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + ka_lane + kb * 32 * kKRow + 16 * ds);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[kb][qb], 0, 0, 0);
-      }
+      for (int qb = 0; qb < 2; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[qb], 0, 0, 0);
     }
-
-    // Keys past S_kv in the last tile take no part.
-    if ((t + 1) * kBlockN > Skv) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * kBlockN + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-          if (key >= Skv) {
-            s[kb][0][r] = kNegInf;
-            s[kb][1][r] = kNegInf;
-          }
-        }
-    }
-
-    // ---- Tile maximum per query (log2 units).
-    float mx[2];
+  };
+  // P = exp2(s * c - m_ref) of one half, packed to bf16.
+  auto softmax_exp = [&](f32x16 (&s)[2], int half) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float m = s[0][qb][0];
+      const float nb = -mref[qb];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int s2 = 0; s2 < 2; ++s2) {
+        f32x8 e;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, s[kb][qb][r]);
-      mx[qb] = max_halves(m) * c;
-    }
-
-    bool keep = true;
-    if (kSkip) {
-      const bool need = (qvalid0 && !(mx[0] - mrun[0] < p.log2_lambda)) ||
-                        (qvalid1 && !(mx[1] - mrun[1] < p.log2_lambda));
-      keep = (t == 0) || __any(need);
-      if (keep) {
-        mrun[0] = fmaxf(mrun[0], mx[0]);
-        mrun[1] = fmaxf(mrun[1], mx[1]);
-      } else {
-        ++skipped;
+        for (int j = 0; j < 8; ++j) e[j] = exp2_fast(__builtin_fmaf(s[qb][8 * s2 + j], c, nb));
+        pf[half][s2][qb] = __builtin_convertvector(e, bf16x8);
       }
-      if (bitmap_row != nullptr && lane == 0) bitmap_row[t] = keep ? 0 : 1;
     }
-
-    if (keep) {
-      // ---- Lazy rescale of the running state.
-      if (__any(mx[0] > mref[0] + kRescaleSlack || mx[1] > mref[1] + kRescaleSlack)) {
+  };
+  // BMM2 of one half: O^T += V^T P^T (16 MFMAs, 16 transposing LDS reads).
+  auto bmm2 = [&](const uint8_t* vs, int half) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const float mnew = fmaxf(mref[qb], mx[qb]);
-          const float alpha = exp2_fast(mref[qb] - mnew);
-          mref[qb] = mnew;
-          lsum[qb] *= alpha;
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db) {
+        const int off = (32 * half + 16 * s2) * kRowBytes + 128 * (db >> 1);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off + 4 * kRowBytes));
+        const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[half][s2][qb], o[db][qb], 0, 0, 0);
+      }
+  };
+  // Row sums of the packed P of one half (the values BMM2 multiplies).
+  auto rowsum = [&](int half) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float acc = lsum[qb];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(pf[half][s2][qb], j), ones, acc, false);
+      lsum[qb] = acc;
+    }
+  };
+  // Half-tile maximum per query in log2 units; keys past S_kv are masked first.
+  auto rowmax = [&](f32x16 (&s)[2], int key0, float (&mx)[2]) {
+    if (key0 + 32 > Skv) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (key >= Skv) {
+          s[0][r] = kNegInf;
+          s[1][r] = kNegInf;
         }
       }
-
-      // ---- P = exp2(s * c - m_ref), packed to bf16 as the BMM2 B operand.
-      bf16x8 pf[2][2][2];  // [kb][16-key step][qb]
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float m = s[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][r]);
+      mx[qb] = max_halves(m) * c;
+    }
+  };
+  // ---- Interleaved blocks of the dense pipeline.  Each MFMA is followed by
+  // its share of independent VALU work and a scheduling fence, so the matrix
+  // core and the vector ALU run side by side; LDS fragments are read two
+  // MFMA steps ahead.
+  auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
+  auto kfrag = [&](const uint8_t* ks, int kb, int ds) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(ks + ka[ds & 3] + kb * 32 * kRowBytes + 128 * (ds >> 2));
+  };
+  auto vfrag = [&](const uint8_t* vs, int half, int step) -> bf16x8 {
+    const int s2 = step >> 2, db = step & 3;
+    const int off = (32 * half + 16 * s2) * kRowBytes + 128 * (db >> 1);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off + 4 * kRowBytes));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4,
+                                   5, 6, 7);
+  };
+  // exp of element pair k (0..15) of a half: qb = k / 8, 16-key step s2 = (k / 4) % 2, pair k % 4.
+  auto exp_pair = [&](const f32x16 (&s)[2], int half, int k) {
+    const int qb = k >> 3, s2 = (k >> 2) & 1, jp = k & 3;
+    const float e0 = exp2_fast(__builtin_fmaf(s[qb][8 * s2 + 2 * jp], c, -mref[qb]));
+    const float e1 = exp2_fast(__builtin_fmaf(s[qb][8 * s2 + 2 * jp + 1], c, -mref[qb]));
+    i32x4 w = __builtin_bit_cast(i32x4, pf[half][s2][qb]);
+    const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+    int word = __builtin_bit_cast(int, pr);
+    asm volatile("" : "+v"(word));   // keep the exponentials at this point of the schedule
+    w[jp] = word;
+    pf[half][s2][qb] = __builtin_bit_cast(bf16x8, w);
+  };
+  // A / C: sdst = BMM1(ks, kb) || exponentials of ssrc (half hsrc).
+  auto block_bmm1_exp = [&](const uint8_t* ks, int kb, f32x16 (&sdst)[2], const f32x16 (&ssrc)[2], int hsrc) {
+    bf16x8 kfr[3];
+    kfr[0] = kfrag(ks, kb, 0);
+    kfr[1] = kfrag(ks, kb, 1);
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      if (ds + 2 < 8) kfr[(ds + 2) % 3] = kfrag(ks, kb, ds + 2);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const float nb = -mref[qb];
-        float part = 0.0f;
+        if (ds == 0) {
+          f32x16 z;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            f32x8 e;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              e[j] = exp2_fast(__builtin_fmaf(s[kb][qb][8 * s2 + j], c, nb));
-              part += e[j];
-            }
-            pf[kb][s2][qb] = __builtin_convertvector(e, bf16x8);
-          }
-        lsum[qb] += part;
+          for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+          sdst[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[0], qf[qb][0], z, 0, 0, 0);
+        } else {
+          sdst[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ds % 3], qf[qb][ds], sdst[qb], 0, 0, 0);
+        }
+        exp_pair(ssrc, hsrc, 2 * ds + qb);
+        fence();
       }
-
-      // ---- BMM2: O^T += V^T P^T over the tile's 64 keys (4 steps of 16).
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int off = va_lane + (32 * kb + 16 * s2) * kVRow + 32 * db;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (DITATTN_LDS s16x4*)(st + off));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (DITATTN_LDS s16x4*)(st + off + 4 * kVRow));
-            const bf16x4 lo_b = __builtin_bit_cast(bf16x4, lo);
-            const bf16x4 hi_b = __builtin_bit_cast(bf16x4, hi);
-            const bf16x8 a = __builtin_shufflevector(lo_b, hi_b, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-              o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][s2][qb], o[db][qb], 0, 0, 0);
-          }
     }
+  };
+  // B / D: O += BMM2(vs, half) || row max of smax (into mx) and row sums of half hsum.
+  auto block_bmm2_max = [&](const uint8_t* vs, int half, f32x16 (&smax)[2], float (&mx)[2], int hsum) {
+    bf16x8 vfr[3];
+    vfr[0] = vfrag(vs, half, 0);
+    vfr[1] = vfrag(vs, half, 1);
+    float m0 = smax[0][0], m1 = smax[1][0];
+    float acc0 = lsum[0], acc1 = lsum[1];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int step = 0; step < 8; ++step) {
+      if (step + 2 < 8) vfr[(step + 2) % 3] = vfrag(vs, half, step + 2);
+      const int s2 = step >> 2, db = step & 3;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[step % 3], pf[half][s2][qb], o[db][qb], 0, 0, 0);
+        // VALU share: two max steps and one dot2 of the row sums
+        const int r = 2 * step + 1;   // registers 1..15 of smax[qb], two per step
+        if (qb == 0) {
+          m0 = fmaxf(m0, smax[0][r]);
+          if (r + 1 < 16) m0 = fmaxf(m0, smax[0][r + 1]);
+          m1 = fmaxf(m1, smax[1][r]);
+          if (r + 1 < 16) m1 = fmaxf(m1, smax[1][r + 1]);
+        }
+        {
+          const int k = 2 * step + qb;   // dot2 k of 16: qb' = k / 8, s2' = (k / 4) % 2, word k % 4
+          const int qs = k >> 3, ss = (k >> 2) & 1, wd = k & 3;
+          const bf16x2 pr = bf16_pair(pf[hsum][ss][qs], wd);
+          if (qs == 0)
+            acc0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc0, false);
+          else
+            acc1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc1, false);
+        }
+        asm volatile("" : "+v"(m0), "+v"(m1), "+v"(acc0), "+v"(acc1));
+        fence();
+      }
+    }
+    lsum[0] = acc0;
+    lsum[1] = acc1;
+    mx[0] = max_halves(m0) * c;
+    mx[1] = max_halves(m1) * c;
+  };
+  // Tail mask of a half starting at key key0 (keys past S_kv take no part).
+  auto mask_half = [&](f32x16 (&s)[2], int key0) {
+    if (key0 + 32 > Skv) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (key >= Skv) {
+          s[0][r] = kNegInf;
+          s[1][r] = kNegInf;
+        }
+      }
+    }
+  };
+  auto needs_rescale = [&](const float (&mx)[2]) -> bool {
+    return __any(mx[0] > mref[0] + kRescaleSlack || mx[1] > mref[1] + kRescaleSlack);
+  };
+  auto rescale = [&](const float (&mx)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mnew = fmaxf(mref[qb], mx[qb]);
+      const float alpha = exp2_fast(mref[qb] - mnew);
+      mref[qb] = mnew;
+      lsum[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
+    }
+  };
+  // Skip vote for half-tile u (u > 0): kept unless every valid row is below lambda.
+  auto decide = [&](const float (&mx)[2], int u) -> bool {
+    bool keep = true;
+    if (u > 0) {
+      const bool need = (qvalid0 && !(mx[0] - mrun[0] < p.log2_lambda)) ||
+                        (qvalid1 && !(mx[1] - mrun[1] < p.log2_lambda));
+      keep = __any(need);
+    }
+    if (keep) {
+      mrun[0] = fmaxf(mrun[0], mx[0]);
+      mrun[1] = fmaxf(mrun[1], mx[1]);
+    } else {
+      ++skipped;
+    }
+    if (bitmap_row != nullptr && lane == 0) bitmap_row[u] = keep ? 0 : 1;
+    return keep;
+  };
 
-    if (t + 1 < nkt) lstore((t + 1) & 1);
-    __syncthreads();
+  mref[0] = mref[1] = kNegInf;
+  mrun[0] = mrun[1] = kNegInf;
+
+  // ---- Prologue: tiles 0..2 in flight.
+  issue_loads(IC<0>{}, 0);
+  issue_loads(IC<1>{}, 1);
+  issue_loads(IC<2>{}, 2);
+
+  float mx0[2], mx1[2];
+  if constexpr (!kSkip) {
+    // S of the first half of tile 0.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));
+    wg_barrier();
+    bmm1(sK0, 0, s0);
+    rowmax(s0, 0, mx0);
   }
+
+  // ---- One KV tile (two 32-key halves): stage S = j % 4 holds tile j.
+  // Dense: s0 / mx0 of tile j's first half come in from the previous step,
+  // and this step leaves those of tile j+1.  Four blocks, each pairing MFMA
+  // work with independent VALU work:
+  //   A: exp(j, half 0)         || BMM1(j, half 1)
+  //   B: row max (j, half 1)    || BMM2(j, half 0)
+  //   C: exp(j, half 1)         || BMM1(j+1, half 0)
+  //   D: row max (j+1, half 0)  || BMM2(j, half 1)
+  // The rare rescale of the running state sits between the blocks.
+  auto iteration = [&](auto s_c, int j) {
+    constexpr int S = decltype(s_c)::value;
+    const uint8_t* ks = kst(IC<S>{});
+    const uint8_t* vs = vst(IC<S>{});
+    const int key0 = j * kBlockN;
+    if constexpr (!kSkip) {
+      if (needs_rescale(mx0)) rescale(mx0);
+      // A: exp(j, half 0) || BMM1(j, half 1)
+      block_bmm1_exp(ks, 1, s1, s0, 0);
+      // B: BMM2(j, half 0) || row max (j, half 1), row sums (j, half 0)
+      mask_half(s1, key0 + 32);
+      block_bmm2_max(vs, 0, s1, mx1, 0);
+      if (needs_rescale(mx1)) rescale(mx1);
+      // (past the last tile the next stage holds zeros; the extra BMM1 is harmless)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));   // tile j+1 landed (j+2 may be in flight)
+      wg_barrier();
+      issue_loads(IC<(S + 3) & 3>{}, j + 3);
+      // C: exp(j, half 1) || BMM1(j+1, half 0)
+      block_bmm1_exp(kst(IC<(S + 1) & 3>{}), 0, s0, s1, 1);
+      // D: BMM2(j, half 1) || row max (j+1, half 0), row sums (j, half 1)
+      mask_half(s0, key0 + kBlockN);
+      block_bmm2_max(vs, 1, s0, mx0, 1);
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));   // tile j landed (j+1, j+2 may be in flight)
+      wg_barrier();
+      issue_loads(IC<(S + 3) & 3>{}, j + 3);
+      // Skip-Softmax: each 32-key half is a KV tile of its own for the vote.
+      bmm1(ks, 0, s0);
+      rowmax(s0, key0, mx0);
+      const bool keep0 = decide(mx0, 2 * j);
+      if (keep0) {
+        if (needs_rescale(mx0)) rescale(mx0);
+        softmax_exp(s0, 0);
+      }
+      bmm1(ks, 1, s1);
+      rowmax(s1, key0 + 32, mx1);
+      if (keep0) {
+        bmm2(vs, 0);
+        rowsum(0);
+      }
+      if (key0 + 32 < Skv && decide(mx1, 2 * j + 1)) {
+        if (needs_rescale(mx1)) rescale(mx1);
+        softmax_exp(s1, 1);
+        bmm2(vs, 1);
+        rowsum(1);
+      }
+    }
+  };
+
+  for (int j = 0;; j += 4) {
+    iteration(IC<0>{}, j);
+    if (j + 1 >= nkt) break;
+    iteration(IC<1>{}, j + 1);
+    if (j + 2 >= nkt) break;
+    iteration(IC<2>{}, j + 2);
+    if (j + 3 >= nkt) break;
+    iteration(IC<3>{}, j + 3);
+    if (j + 4 >= nkt) break;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   if (kSkip && p.counter != nullptr && lane == 0 && q0 < Sq && skipped)
     atomicAdd(p.counter, (unsigned long long)skipped);

@@ -11,7 +11,8 @@ constexpr int kHeadDim = 128;
 constexpr int kWaveRows = 64;    // query rows owned by one wavefront (skip decision unit)
 constexpr int kWavesPerWG = 4;
 constexpr int kBlockM = kWaveRows * kWavesPerWG;  // query rows per workgroup
-constexpr int kBlockN = 64;       // keys per KV tile
+constexpr int kBlockN = 64;       // keys per KV tile (LDS stage)
+constexpr int kSkipBlockN = 32;   // keys per Skip-Softmax vote (half a KV tile)
 constexpr int kMeanChunk = 256;   // tokens per partial sum of the K mean
 
 struct FmhaBf16Args {

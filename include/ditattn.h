@@ -152,7 +152,8 @@ int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o
 /* Skip-Softmax attention on BF16 ([TA] "Skip-Softmax"; [SSD] knob table:
  * skip_softmax_threshold_scale_factor, threshold = factor / seqlen).
  *   lambda = threshold_factor / S_kv.  Queries are tiled in blocks of
- *   block_m rows and keys in tiles of block_n keys (attn_tile_config).  For
+ *   block_m rows and keys in tiles of block_n keys (attn_tile_config: 64
+ *   rows x 32 keys).  For
  *   each query block, KV tiles are visited in ascending order; tile t > 0 is
  *   skipped when, for every valid row i of the block,
  *   exp(M_it - m_i) < lambda, where M_it is the row's largest logit in the
@@ -175,9 +176,11 @@ int attn_skip_softmax(const void* q, const void* k, const void* v, void* o,
  * INVALID_ARG when t or D is not finite or outside [0, 1]. */
 int attn_skip_gate(float t, float disabled_until_timestep, int* enabled);
 
-/* Query and KV tile sizes of the attention kernels (block_m query rows per
- * skip decision, block_n keys per KV tile).  Host-only. */
-int attn_tile_config(int* block_m, int* block_n);
+/* Tile sizes of the attention kernels: block_m query rows and block_n keys
+ * per Skip-Softmax vote (the skip bitmap's tile), and kv_tile keys per KV
+ * tile of the online softmax (the tile order SAGE's P rounding follows).
+ * Host-only. */
+int attn_tile_config(int* block_m, int* block_n, int* kv_tile);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* attn_last_error(void);

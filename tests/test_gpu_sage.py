@@ -47,7 +47,7 @@ def test_sage_attention_matches_emulation(dt, qb, kb, B, Sq, Skv, Hq, Hkv):
     announce(f"attn_sage {dt} ({qb},{kb}) B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}")
     q, _, _ = gaussian_qkv(B, Sq, Hq, Hkv, seed=Sq)
     _, k, v = gaussian_qkv(B, Skv, Hq, Hkv, seed=Skv + 1, k_bias_std=4.0, outliers=4)
-    _, bn = dit.tile_config()
+    bn = dit.kv_tile()
     rec = dit.SageRecipe(dt, "fp8", qb, kb, 1)
     o = dit.attn_sage(q.cuda(), k.cuda(), v.cuda(), rec, out_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -73,7 +73,8 @@ def test_full_size_sampled(name):
     gpu = dit.sage_quantize(qd, kd, vd, rec)
     torch.cuda.synchronize()
     S = q.shape[1]
-    bm, bn = dit.tile_config()
+    bm, _ = dit.tile_config()
+    bn = dit.kv_tile()
     nqt = -(-S // bm)
     qtiles = [0, nqt // 3, nqt - 1]
     rows = np.concatenate([np.arange(t * bm, min(S, t * bm + bm)) for t in qtiles])
