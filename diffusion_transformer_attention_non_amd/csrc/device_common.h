@@ -30,6 +30,45 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Raw buffer resource (stride 0) over [base, base + num_records): loads at
+// offsets past num_records return zero.  Every field is made wave-uniform so
+// the descriptor lives in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_records);
+  r[3] = 0x00020000;   // 32-bit data format, no swizzle
+  return r;
+}
+
+// buffer_load_dwordx4 ... lds: lane l reads 16 bytes at voffset and the wave
+// writes them to LDS bytes [lds_addr + 16 l, lds_addr + 16 l + 16).  Issued
+// as inline assembly, so the compiler tracks no LDS dependency for it and
+// inserts no wait of its own; the caller orders it against LDS reads with an
+// explicit s_waitcnt vmcnt and a barrier.  lds_addr must be wave-uniform.
+// (m0 is a reserved register: the compiler sets it before each of its own
+// uses, so clobbering it here is safe; the warning about that is silenced.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of a __shared__ object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((DITATTN_LDS T*)p);
+}
+
 __device__ __forceinline__ uint4 ldg16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

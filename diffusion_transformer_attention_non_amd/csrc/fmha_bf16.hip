@@ -58,7 +58,7 @@ constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the reference ma
 constexpr int kRowBytes = kHeadDim * 2;                 // one bf16 row of 128 channels
 constexpr int kTileBytes = kBlockN * kRowBytes;         // 16 KB per K or V tile
 constexpr int kLoadsPerTile = 8;                        // buffer->LDS loads per wavefront per tile
-constexpr int kBufferFlags = 0x00020000;                // raw buffer, 32-bit data format
+constexpr int kPrefetch = 2;                            // LDS fragments are read this many MFMA steps ahead
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -109,12 +109,12 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV3[kTileBytes];
-  auto kst = [&](auto s) -> uint8_t* {
+  auto kst = [&](auto s) __attribute__((always_inline)) -> uint8_t* {
     constexpr int S = decltype(s)::value;
     if constexpr (S == 0) return sK0; else if constexpr (S == 1) return sK1;
     else if constexpr (S == 2) return sK2; else return sK3;
   };
-  auto vst = [&](auto s) -> uint8_t* {
+  auto vst = [&](auto s) __attribute__((always_inline)) -> uint8_t* {
     constexpr int S = decltype(s)::value;
     if constexpr (S == 0) return sV0; else if constexpr (S == 1) return sV1;
     else if constexpr (S == 2) return sV2; else return sV3;
@@ -155,10 +155,8 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   const uint32_t kstride = (uint32_t)(p.ks[1] * 2), vstride = (uint32_t)(p.vs[1] * 2);
   const char* kbase = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.k) + b * p.ks[0] + g * p.ks[2]);
   const char* vbase = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.v) + b * p.vs[0] + g * p.vs[2]);
-  const __amdgpu_buffer_rsrc_t krsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)(kstride * (uint32_t)Skv), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)(vstride * (uint32_t)Skv), kBufferFlags);
+  const i32x4 krsrc = make_rsrc(kbase, kstride * (uint32_t)Skv);
+  const i32x4 vrsrc = make_rsrc(vbase, vstride * (uint32_t)Skv);
 
   // Load slots: round i (0..3) of the workgroup covers LDS bytes [4096 i, 4096 i + 4096);
   // lane fills 16-byte slot 256 i + 64 wave + lane = row 16 i + 4 wave + lane/16, chunk lane%16.
@@ -171,16 +169,15 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     koff[i] = (uint32_t)kkey * kstride + 16u * (uint32_t)(pch ^ (r & 7));
     voff[i] = (uint32_t)r * vstride + 16u * (uint32_t)(pch ^ (2 * (r & 3)));
   }
-  auto issue_loads = [&](auto s, int t) {
+  const uint32_t wave_slot = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * wave);
+  auto issue_loads = [&](auto s, int t) __attribute__((always_inline)) {
     const uint32_t tk = (uint32_t)t * kBlockN * kstride, tv = (uint32_t)t * kBlockN * vstride;
-    uint8_t* kd = kst(s) + 1024 * wave;
-    uint8_t* vd = vst(s) + 1024 * wave;
+    const uint32_t kd = lds_addr(kst(s)) + wave_slot;
+    const uint32_t vd = lds_addr(vst(s)) + wave_slot;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (DITATTN_LDS void*)(kd + 4096 * i), 16, koff[i] + tk, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) buffer_load_lds16(krsrc, kd + 4096 * i, koff[i] + tk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (DITATTN_LDS void*)(vd + 4096 * i), 16, voff[i] + tv, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) buffer_load_lds16(vrsrc, vd + 4096 * i, voff[i] + tv);
   };
 
   // ---- LDS read addresses (lane constants; the rest is immediate).
@@ -220,7 +217,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   bf16x8 pf[2][2][2];    // P^T of the tile, [half][16-key step][qb]
 
   // BMM1 of one 32-key half from K stage ks (16 MFMAs, 8 LDS reads).
-  auto bmm1 = [&](const uint8_t* ks, int kb, f32x16 (&s)[2]) {
+  auto bmm1 = [&](const uint8_t* ks, int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -234,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     }
   };
   // P = exp2(s * c - m_ref) of one half, packed to bf16.
-  auto softmax_exp = [&](f32x16 (&s)[2], int half) {
+  auto softmax_exp = [&](f32x16 (&s)[2], int half) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float nb = -mref[qb];
@@ -248,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     }
   };
   // BMM2 of one half: O^T += V^T P^T (16 MFMAs, 16 transposing LDS reads).
-  auto bmm2 = [&](const uint8_t* vs, int half) {
+  auto bmm2 = [&](const uint8_t* vs, int half) __attribute__((always_inline)) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -265,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
       }
   };
   // Row sums of the packed P of one half (the values BMM2 multiplies).
-  auto rowsum = [&](int half) {
+  auto rowsum = [&](int half) __attribute__((always_inline)) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -279,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     }
   };
   // Half-tile maximum per query in log2 units; keys past S_kv are masked first.
-  auto rowmax = [&](f32x16 (&s)[2], int key0, float (&mx)[2]) {
+  auto rowmax = [&](f32x16 (&s)[2], int key0, float (&mx)[2]) __attribute__((always_inline)) {
     if (key0 + 32 > Skv) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -298,15 +295,21 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
       mx[qb] = max_halves(m) * c;
     }
   };
-  // ---- Interleaved blocks of the dense pipeline.  Each MFMA is followed by
-  // its share of independent VALU work and a scheduling fence, so the matrix
-  // core and the vector ALU run side by side; LDS fragments are read two
-  // MFMA steps ahead.
-  auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
-  auto kfrag = [&](const uint8_t* ks, int kb, int ds) -> bf16x8 {
+  // ---- Dense pipeline.  A half-tile (32 keys) goes through BMM1 (S), the row
+  // maximum, 16 exponential pairs (P) and BMM2.  Two 16-MFMA blocks per half
+  // carry its VALU work:
+  //   Q block of half u: BMM2(u-1) || row max of S(u), exponential pairs 0-6 of S(u)
+  //   P block of half u: BMM1(u+1) || exponential pairs 7-15 of S(u)
+  // The exponentials of the Q block are taken with the reference maximum as
+  // it stands (speculatively); the check after the block redoes them in the
+  // rare case the reference has to move.  Every pair runs a three-stage
+  // pipeline over consecutive MFMA slots (scale and shift, exp2, pack to bf16
+  // and add to the row sum), so no slot waits on its own results.
+  auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+  auto kfrag = [&](const uint8_t* ks, int kb, int ds) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(ks + ka[ds & 3] + kb * 32 * kRowBytes + 128 * (ds >> 2));
   };
-  auto vfrag = [&](const uint8_t* vs, int half, int step) -> bf16x8 {
+  auto vfrag = [&](const uint8_t* vs, int half, int step) __attribute__((always_inline)) -> bf16x8 {
     const int s2 = step >> 2, db = step & 3;
     const int off = (32 * half + 16 * s2) * kRowBytes + 128 * (db >> 1);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off));
@@ -315,84 +318,121 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4,
                                    5, 6, 7);
   };
-  // exp of element pair k (0..15) of a half: qb = k / 8, 16-key step s2 = (k / 4) % 2, pair k % 4.
-  auto exp_pair = [&](const f32x16 (&s)[2], int half, int k) {
-    const int qb = k >> 3, s2 = (k >> 2) & 1, jp = k & 3;
-    const float e0 = exp2_fast(__builtin_fmaf(s[qb][8 * s2 + 2 * jp], c, -mref[qb]));
-    const float e1 = exp2_fast(__builtin_fmaf(s[qb][8 * s2 + 2 * jp + 1], c, -mref[qb]));
-    i32x4 w = __builtin_bit_cast(i32x4, pf[half][s2][qb]);
-    const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-    int word = __builtin_bit_cast(int, pr);
-    asm volatile("" : "+v"(word));   // keep the exponentials at this point of the schedule
-    w[jp] = word;
-    pf[half][s2][qb] = __builtin_bit_cast(bf16x8, w);
-  };
-  // A / C: sdst = BMM1(ks, kb) || exponentials of ssrc (half hsrc).
-  auto block_bmm1_exp = [&](const uint8_t* ks, int kb, f32x16 (&sdst)[2], const f32x16 (&ssrc)[2], int hsrc) {
-    bf16x8 kfr[3];
-    kfr[0] = kfrag(ks, kb, 0);
-    kfr[1] = kfrag(ks, kb, 1);
+  // 16 MFMA slots of BMM1 (half kb of K stage ks into sdst); valu(t) runs after slot t's MFMA.
+  auto bmm1_block = [&](const uint8_t* ks, int kb, f32x16 (&sdst)[2], auto&& valu) __attribute__((always_inline)) {
+    bf16x8 kfr[kPrefetch + 1];
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
-      if (ds + 2 < 8) kfr[(ds + 2) % 3] = kfrag(ks, kb, ds + 2);
+    for (int i = 0; i < kPrefetch; ++i) kfr[i] = kfrag(ks, kb, i);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (ds == 0) {
-          f32x16 z;
+    for (int t = 0; t < 16; ++t) {
+      const int ds = t >> 1, qb = t & 1;
+      if (qb == 0 && ds + kPrefetch < 8) kfr[(ds + kPrefetch) % (kPrefetch + 1)] = kfrag(ks, kb, ds + kPrefetch);
+      if (ds == 0) {
+        f32x16 z;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) z[r] = 0.0f;
-          sdst[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[0], qf[qb][0], z, 0, 0, 0);
-        } else {
-          sdst[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ds % 3], qf[qb][ds], sdst[qb], 0, 0, 0);
-        }
-        exp_pair(ssrc, hsrc, 2 * ds + qb);
-        fence();
+        for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+        sdst[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[0], qf[qb][0], z, 0, 0, 0);
+      } else {
+        sdst[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ds % (kPrefetch + 1)], qf[qb][ds], sdst[qb], 0, 0, 0);
       }
+      valu(t);
+      fence();
     }
   };
-  // B / D: O += BMM2(vs, half) || row max of smax (into mx) and row sums of half hsum.
-  auto block_bmm2_max = [&](const uint8_t* vs, int half, f32x16 (&smax)[2], float (&mx)[2], int hsum) {
-    bf16x8 vfr[3];
-    vfr[0] = vfrag(vs, half, 0);
-    vfr[1] = vfrag(vs, half, 1);
-    float m0 = smax[0][0], m1 = smax[1][0];
-    float acc0 = lsum[0], acc1 = lsum[1];
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // 16 MFMA slots of BMM2 (O^T += V^T P^T for half `half` of V stage vs).
+  auto bmm2_block = [&](const uint8_t* vs, int half, const bf16x8 (&pin)[2][2], auto&& valu) __attribute__((always_inline)) {
+    bf16x8 vfr[kPrefetch + 1];
 #pragma unroll
-    for (int step = 0; step < 8; ++step) {
-      if (step + 2 < 8) vfr[(step + 2) % 3] = vfrag(vs, half, step + 2);
+    for (int i = 0; i < kPrefetch; ++i) vfr[i] = vfrag(vs, half, i);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int step = t >> 1, qb = t & 1;
       const int s2 = step >> 2, db = step & 3;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[step % 3], pf[half][s2][qb], o[db][qb], 0, 0, 0);
-        // VALU share: two max steps and one dot2 of the row sums
-        const int r = 2 * step + 1;   // registers 1..15 of smax[qb], two per step
-        if (qb == 0) {
-          m0 = fmaxf(m0, smax[0][r]);
-          if (r + 1 < 16) m0 = fmaxf(m0, smax[0][r + 1]);
-          m1 = fmaxf(m1, smax[1][r]);
-          if (r + 1 < 16) m1 = fmaxf(m1, smax[1][r + 1]);
-        }
-        {
-          const int k = 2 * step + qb;   // dot2 k of 16: qb' = k / 8, s2' = (k / 4) % 2, word k % 4
-          const int qs = k >> 3, ss = (k >> 2) & 1, wd = k & 3;
-          const bf16x2 pr = bf16_pair(pf[hsum][ss][qs], wd);
-          if (qs == 0)
-            acc0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc0, false);
-          else
-            acc1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc1, false);
-        }
-        asm volatile("" : "+v"(m0), "+v"(m1), "+v"(acc0), "+v"(acc1));
-        fence();
-      }
+      if (qb == 0 && step + kPrefetch < 8) vfr[(step + kPrefetch) % (kPrefetch + 1)] = vfrag(vs, half, step + kPrefetch);
+      o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[step % (kPrefetch + 1)], pin[s2][qb], o[db][qb], 0, 0, 0);
+      valu(t);
+      fence();
     }
-    lsum[0] = acc0;
-    lsum[1] = acc1;
-    mx[0] = max_halves(m0) * c;
-    mx[1] = max_halves(m1) * c;
+  };
+  // Exponential pipeline, pair k (0..15) of a half: qb = k / 8, 16-key step
+  // s2 = (k / 4) % 2, register pair k % 4 of that step.
+  float ex[3][2];       // pairs in flight, slot k % 3
+  float lp[2][2];       // partial row sums of the half in flight, [qb][even/odd key]
+  auto pair_stage = [&](int stage, const f32x16 (&sv)[2], bf16x8 (&pout)[2][2], int k) __attribute__((always_inline)) {
+    const int qb = k >> 3, s2 = (k >> 2) & 1, jp = k & 3;
+    float(&x)[2] = ex[k % 3];
+    if (stage == 0) {
+      x[0] = __builtin_fmaf(sv[qb][8 * s2 + 2 * jp], c, -mref[qb]);
+      x[1] = __builtin_fmaf(sv[qb][8 * s2 + 2 * jp + 1], c, -mref[qb]);
+      asm volatile("" : "+v"(x[0]), "+v"(x[1]));
+    } else if (stage == 1) {
+      x[0] = exp2_fast(x[0]);
+      x[1] = exp2_fast(x[1]);
+      asm volatile("" : "+v"(x[0]), "+v"(x[1]));
+    } else {
+      lp[qb][0] += x[0];
+      lp[qb][1] += x[1];
+      i32x4 w = __builtin_bit_cast(i32x4, pout[s2][qb]);
+      const bf16x2 pr = {(__bf16)x[0], (__bf16)x[1]};
+      int word = __builtin_bit_cast(int, pr);
+      asm volatile("" : "+v"(word), "+v"(lp[qb][0]), "+v"(lp[qb][1]));
+      w[jp] = word;
+      pout[s2][qb] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  // Row maximum of a half, one step per slot: i = 0..15 (qb = i / 8).
+  float mpart[2];
+  auto max_stage = [&](const f32x16 (&sv)[2], int i) __attribute__((always_inline)) {
+    const int qb = i >> 3, r = i & 7;
+    if (r == 0)
+      mpart[qb] = fmaxf(fmaxf(sv[qb][0], sv[qb][1]), sv[qb][2]);
+    else if (r < 7)
+      mpart[qb] = fmaxf(fmaxf(mpart[qb], sv[qb][2 * r + 1]), sv[qb][2 * r + 2]);
+    else
+      mpart[qb] = fmaxf(mpart[qb], sv[qb][15]);
+  };
+  // VALU work of a Q block: max step t, and pairs 0..6 at slots 2k (fma), 2k+1 (exp), 2k+2 (pack).
+  auto q_valu = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2], int t) __attribute__((always_inline)) {
+    max_stage(sv, t);
+    if (t == 0) {
+      lp[0][0] = lp[0][1] = lp[1][0] = lp[1][1] = 0.0f;
+    }
+    if ((t & 1) == 0 && t >= 2) pair_stage(2, sv, pout, (t - 2) >> 1);
+    if ((t & 1) == 1) pair_stage(1, sv, pout, (t - 1) >> 1);
+    if ((t & 1) == 0 && t <= 12) pair_stage(0, sv, pout, t >> 1);
+  };
+  // VALU work of a P block: pairs 7..15 with their scale-and-shift at these slots.
+  auto p_valu = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2], int t) __attribute__((always_inline)) {
+    constexpr int f[9] = {0, 1, 3, 5, 7, 8, 10, 12, 13};
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      if (t == f[i] + 2) pair_stage(2, sv, pout, 7 + i);
+      if (t == f[i] + 1) pair_stage(1, sv, pout, 7 + i);
+      if (t == f[i]) pair_stage(0, sv, pout, 7 + i);
+    }
+  };
+  // Row maximum in log2 units from the block's partial maxima.
+  auto finish_max = [&](float (&mx)[2]) __attribute__((always_inline)) {
+    mx[0] = max_halves(mpart[0]) * c;
+    mx[1] = max_halves(mpart[1]) * c;
+  };
+  // Slow path after a Q block whose maximum moved the reference: rescale the
+  // running state, then redo pairs 0..6 with the new reference.
+  auto redo_q_pairs = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2]) __attribute__((always_inline)) {
+    lp[0][0] = lp[0][1] = lp[1][0] = lp[1][1] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      pair_stage(0, sv, pout, k);
+      pair_stage(1, sv, pout, k);
+      pair_stage(2, sv, pout, k);
+    }
+  };
+  auto add_row_sums = [&]() __attribute__((always_inline)) {
+    lsum[0] += lp[0][0] + lp[0][1];
+    lsum[1] += lp[1][0] + lp[1][1];
   };
   // Tail mask of a half starting at key key0 (keys past S_kv take no part).
-  auto mask_half = [&](f32x16 (&s)[2], int key0) {
+  auto mask_half = [&](f32x16 (&s)[2], int key0) __attribute__((always_inline)) {
     if (key0 + 32 > Skv) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -404,10 +444,10 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
       }
     }
   };
-  auto needs_rescale = [&](const float (&mx)[2]) -> bool {
+  auto needs_rescale = [&](const float (&mx)[2]) __attribute__((always_inline)) -> bool {
     return __any(mx[0] > mref[0] + kRescaleSlack || mx[1] > mref[1] + kRescaleSlack);
   };
-  auto rescale = [&](const float (&mx)[2]) {
+  auto rescale = [&](const float (&mx)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float mnew = fmaxf(mref[qb], mx[qb]);
@@ -421,7 +461,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     }
   };
   // Skip vote for half-tile u (u > 0): kept unless every valid row is below lambda.
-  auto decide = [&](const float (&mx)[2], int u) -> bool {
+  auto decide = [&](const float (&mx)[2], int u) __attribute__((always_inline)) -> bool {
     bool keep = true;
     if (u > 0) {
       const bool need = (qvalid0 && !(mx[0] - mrun[0] < p.log2_lambda)) ||
@@ -447,45 +487,64 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   issue_loads(IC<2>{}, 2);
 
   float mx0[2], mx1[2];
+  f32x16 sb[2][2];       // dense: S^T of two halves in flight, [buffer][qb]
+  bf16x8 pb[2][2][2];    // dense: P^T of two halves in flight, [buffer][16-key step][qb]
+  auto q_check = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2]) __attribute__((always_inline)) {
+    float mx[2];
+    finish_max(mx);
+    if (needs_rescale(mx)) {
+      rescale(mx);
+      redo_q_pairs(sv, pout);
+    }
+  };
   if constexpr (!kSkip) {
-    // S of the first half of tile 0.
+    // S of half 0 (tile 0), then its Q-block VALU work with no BMM2 to pair with.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));
     wg_barrier();
-    bmm1(sK0, 0, s0);
-    rowmax(s0, 0, mx0);
+    bmm1_block(sK0, 0, sb[0], [](int) {});
+    mask_half(sb[0], 0);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) q_valu(sb[0], pb[0], t);
+    q_check(sb[0], pb[0]);
   }
 
-  // ---- One KV tile (two 32-key halves): stage S = j % 4 holds tile j.
-  // Dense: s0 / mx0 of tile j's first half come in from the previous step,
-  // and this step leaves those of tile j+1.  Four blocks, each pairing MFMA
-  // work with independent VALU work:
-  //   A: exp(j, half 0)         || BMM1(j, half 1)
-  //   B: row max (j, half 1)    || BMM2(j, half 0)
-  //   C: exp(j, half 1)         || BMM1(j+1, half 0)
-  //   D: row max (j+1, half 0)  || BMM2(j, half 1)
-  // The rare rescale of the running state sits between the blocks.
-  auto iteration = [&](auto s_c, int j) {
+  // ---- One KV tile (halves u0 = 2j, u1 = 2j+1): stage S = j % 4 holds tile j.
+  // Dense: S(u0) and the Q-block work on it come in from the previous step.
+  //   P(u0): BMM1(u1)          || pairs 7-15 of S(u0)
+  //   Q(u1): BMM2(u0)          || row max and pairs 0-6 of S(u1), then the check
+  //   P(u1): BMM1(tile j+1, 0) || pairs 7-15 of S(u1)
+  //   Q(u2): BMM2(u1)          || row max and pairs 0-6 of S(tile j+1, 0), then the check
+  // Past the last tile the stages hold zeros and the keys are masked, so the
+  // extra BMM1 and Q-block work change nothing.
+  auto iteration = [&](auto s_c, int j) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
     const uint8_t* ks = kst(IC<S>{});
     const uint8_t* vs = vst(IC<S>{});
     const int key0 = j * kBlockN;
     if constexpr (!kSkip) {
-      if (needs_rescale(mx0)) rescale(mx0);
-      // A: exp(j, half 0) || BMM1(j, half 1)
-      block_bmm1_exp(ks, 1, s1, s0, 0);
-      // B: BMM2(j, half 0) || row max (j, half 1), row sums (j, half 0)
-      mask_half(s1, key0 + 32);
-      block_bmm2_max(vs, 0, s1, mx1, 0);
-      if (needs_rescale(mx1)) rescale(mx1);
-      // (past the last tile the next stage holds zeros; the extra BMM1 is harmless)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));   // tile j+1 landed (j+2 may be in flight)
       wg_barrier();
-      issue_loads(IC<(S + 3) & 3>{}, j + 3);
-      // C: exp(j, half 1) || BMM1(j+1, half 0)
-      block_bmm1_exp(kst(IC<(S + 1) & 3>{}), 0, s0, s1, 1);
-      // D: BMM2(j, half 1) || row max (j+1, half 0), row sums (j, half 1)
-      mask_half(s0, key0 + kBlockN);
-      block_bmm2_max(vs, 1, s0, mx0, 1);
+      // Tile j+3 goes into the stage tile j-1 used (every wavefront is past
+      // it now): K loads ride in the first block, V loads in the second.
+      const uint32_t tk = (uint32_t)(j + 3) * kBlockN * kstride, tv = (uint32_t)(j + 3) * kBlockN * vstride;
+      const uint32_t kd = lds_addr(kst(IC<(S + 3) & 3>{})) + wave_slot;
+      const uint32_t vd = lds_addr(vst(IC<(S + 3) & 3>{})) + wave_slot;
+      bmm1_block(ks, 1, sb[1], [&](int t) __attribute__((always_inline)) {
+        p_valu(sb[0], pb[0], t);
+        if ((t & 3) == 2) buffer_load_lds16(krsrc, kd + 4096 * (t >> 2), koff[t >> 2] + tk);
+      });
+      add_row_sums();
+      mask_half(sb[1], key0 + 32);
+      bmm2_block(vs, 0, pb[0], [&](int t) __attribute__((always_inline)) {
+        q_valu(sb[1], pb[1], t);
+        if ((t & 3) == 2) buffer_load_lds16(vrsrc, vd + 4096 * (t >> 2), voff[t >> 2] + tv);
+      });
+      q_check(sb[1], pb[1]);
+      bmm1_block(kst(IC<(S + 1) & 3>{}), 0, sb[0], [&](int t) __attribute__((always_inline)) { p_valu(sb[1], pb[1], t); });
+      add_row_sums();
+      mask_half(sb[0], key0 + kBlockN);
+      bmm2_block(vs, 1, pb[1], [&](int t) __attribute__((always_inline)) { q_valu(sb[0], pb[0], t); });
+      q_check(sb[0], pb[0]);
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));   // tile j landed (j+1, j+2 may be in flight)
       wg_barrier();
