@@ -61,6 +61,17 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds_addr,
       : "s"(lds_addr), "v"(voffset), "s"(rsrc)
       : "memory", "m0");
 }
+
+// As buffer_load_lds16 with 4 bytes per lane: LDS bytes [lds_addr + 4 l, lds_addr + 4 l + 4).
+__device__ __forceinline__ void buffer_load_lds4(i32x4 rsrc, uint32_t lds_addr, uint32_t voffset) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // LDS byte address of a __shared__ object.

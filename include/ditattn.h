@@ -140,11 +140,12 @@ int sage_quantize(const void* q, const void* k, const void* v, const attn_shape*
 /* SAGE attention ([TA] "SAGE quantization": both matmuls in low precision;
  * [SSD] knob table: sage_block_sizes, bmm1_scale / bmm2_scale).
  *   Runs sage_quantize into ws, then attention on the codes:
- *   s_ij = sm_scale * sq_i * sk_j * <qc_i, kc_j>; online softmax over KV
- *   tiles of 64 keys in ascending order; P enters BMM2 as E4M3(2^8 * p) with
- *   p relative to the running maximum; the row sum takes the unrounded p;
- *   O = acc * sv_d / (2^8 * l).  o_dtype BF16 or FP32.  Errors as
- *   sage_quantize. */
+ *   L_ij = log2(e) * sm_scale * sq_i * sk_j * <qc_i, kc_j>; online softmax
+ *   over KV tiles of 64 keys in ascending order with a power-of-two reference
+ *   M = ceil(running max of L) (an integer); P enters BMM2 as
+ *   p~ = E4M3(2^(L - M + 8)); the row sum adds the same p~; every change of
+ *   M rescales by an exact power of two; O = acc * sv_d / l.  o_dtype BF16 or
+ *   FP32.  Errors as sage_quantize. */
 int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
               const attn_shape* shape, const attn_recipe* recipe, float sm_scale,
               void* ws, size_t ws_bytes, void* stream);

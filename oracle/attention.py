@@ -38,6 +38,8 @@ import numpy as np
 
 from .codecs import E4M3_MAX, INT8_MAX, e4m3_decode, e4m3_encode, f32, int8_code, bf16_round
 
+LOG2E = 1.0 / math.log(2.0)
+
 MEAN_CHUNK = 256
 _ROW_CHUNK_ELEMS = 1 << 25
 
@@ -234,12 +236,15 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
       * BMM1 scale: s_ij = sm_scale * sq(i) * sk(j) * <qc_i, kc_j>, the dot
         exact (int8 or E4M3 codes).
       * KV tiles of ``block_n`` keys in ascending order with an online
-        softmax: M = max_j s_ij over the tile, m' = max(m, M),
-        alpha = exp(m - m'), p_ij = exp(s_ij - m').
-      * P enters BMM2 as E4M3(2**8 * p) (``quantize_p``); the row sum l takes
-        the unrounded p: l = alpha * l + sum_j p_ij.
+        softmax whose reference is a power of two: in log2 units
+        L_ij = s_ij * log2(e), the reference is M = ceil(max L) over the
+        tiles so far (an integer), alpha = 2**(M_old - M), and
+        p_ij = 2**(L_ij - M), so p <= 1 and every rescale is exact.
+      * P enters BMM2 as p~ = E4M3(2**8 * p) (``quantize_p``), and the row
+        sum adds the same values BMM2 multiplies: l = alpha * l + sum_j p~_ij,
+        so the output is a convex combination of the dequantized V rows.
       * acc_d = alpha * acc_d + sum_j p~_ij * dec(vc_jd);
-        O_id = acc_d * sv_d / (2**8 * l_i).
+        O_id = acc_d * sv_d / l_i.
     Returns O [B, R, Hq, D] (float64 unless ``out_dtype`` rounds it).
     """
     dt = quant["qk_dtype"]
@@ -261,20 +266,20 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
             for h in range(g * G, (g + 1) * G):
                 qc = _decode(qc_all[b, h][rows], dt)
                 sq = quant["q_scale"][b, h][rows // qb].astype(np.float64)
-                s = sm_scale * sq[:, None] * sk[None, :] * (qc @ kc.T)
+                s = sm_scale * sq[:, None] * sk[None, :] * (qc @ kc.T) * LOG2E
                 m = np.full(R, -np.inf)
                 l = np.zeros(R)
                 acc = np.zeros((R, D))
                 for t0 in range(0, Skv, block_n):
                     st = s[:, t0:t0 + block_n]
-                    m2 = np.maximum(m, st.max(axis=1))
-                    alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m2))
-                    p = np.exp(st - m2[:, None])
+                    m2 = np.maximum(m, np.ceil(st.max(axis=1)))
+                    alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - m2))
+                    p = np.exp2(st - m2[:, None])
                     pq = e4m3_decode(e4m3_encode(p_scale * p)) if quantize_p else p_scale * p
-                    l = alpha * l + p.sum(axis=1)
+                    l = alpha * l + pq.sum(axis=1)
                     acc = alpha[:, None] * acc + pq @ vd[t0:t0 + block_n]
                     m = m2
-                out[b, :, h, :] = acc * sv[None, :] / (p_scale * l[:, None])
+                out[b, :, h, :] = acc * sv[None, :] / l[:, None]
     return _round_out(out, out_dtype)
 
 

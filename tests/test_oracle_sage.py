@@ -191,7 +191,9 @@ def test_sage_attention_equals_exact_attention_on_exact_codes(dt, qb, kb, Hq, Hk
     sc = 1 / math.sqrt(128)
     got = sage_attention(quant, sc, block_n=64, quantize_p=False)
     ref = exact_attention(q, k, v, sc)
-    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # the SAGE emulation works in log2 units (exp2 of s * log2 e); that extra
+    # float64 multiply per logit moves small outputs by a few 1e-11 relative
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
 
 
 def test_sage_attention_zero_q_closed_form():
@@ -202,6 +204,21 @@ def test_sage_attention_zero_q_closed_form():
     ref = quant["v_scale"][0, 0].astype(np.float64) * e4m3_decode(quant["v_codes"][0, 0]).mean(axis=0)
     for h in range(2):
         np.testing.assert_allclose(o[0, :, h], np.broadcast_to(ref, (150, 128)), rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("dt,kb", [("int8", 16), ("fp8", 4)])
+def test_sage_attention_constant_v_is_reproduced_exactly(dt, kb):
+    # The row sum adds the rounded P that BMM2 multiplies, so O is a convex
+    # combination of the dequantized V rows: a V whose rows are all equal comes
+    # back unchanged (up to float64 rounding), whatever the P rounding did.
+    q, k, _ = _gauss_inputs(1, 200, 2, 1, 12)
+    row = torch.randn(128, generator=torch.Generator().manual_seed(3))
+    v = row.to(torch.bfloat16)[None, None, None, :].expand(1, 200, 1, 128).contiguous()
+    quant = sage_quantize(q, k, v, dt, 1, kb)
+    o = sage_attention(quant, 1 / math.sqrt(128), block_n=64)
+    vrow = quant["v_scale"][0, 0].astype(np.float64) * e4m3_decode(quant["v_codes"][0, 0][0])
+    np.testing.assert_allclose(o[0, :, 0], np.broadcast_to(vrow, (200, 128)), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(o[0, :, 1], np.broadcast_to(vrow, (200, 128)), rtol=1e-13, atol=1e-15)
 
 
 def test_sage_attention_independent_of_tile_size_without_p_rounding():
@@ -222,4 +239,9 @@ def test_sage_attention_close_to_exact_attention(dt, kb):
     o = sage_attention(quant, sc, block_n=64)
     ref = exact_attention(q, k, v, sc)
     rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
-    assert rel < 0.05, rel
+    # Q/K quantization alone gives ~0.044 on these inputs; the E4M3 P (row
+    # maximum of 2^8 p in (128, 256] under the power-of-two reference) adds ~0.024
+    # in quadrature
+    assert rel < 0.06, rel
+    rel_nop = np.linalg.norm(sage_attention(quant, sc, block_n=64, quantize_p=False) - ref) / np.linalg.norm(ref)
+    assert rel_nop < rel
