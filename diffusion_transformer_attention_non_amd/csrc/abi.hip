@@ -288,7 +288,7 @@ int attn_dense_bf16(const void* q, const void* k, const void* v, void* o, attn_d
   if ((rc = check_kv_span(shape))) return rc;
   if ((rc = check_ptrs(q, k, v, o))) return rc;
   const FmhaBf16Args a = bf16_args(q, k, v, o, o_dtype, shape, sm_scale);
-  return launched(launch_fmha_bf16(a, false, static_cast<hipStream_t>(stream)), "dense attention");
+  return launched(launch_fmha_bf16(a, static_cast<hipStream_t>(stream)), "dense attention");
 }
 
 int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
@@ -319,12 +319,12 @@ int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn
       const size_t n = (size_t)(shape->B * shape->Hq * nqb * nkt);
       if ((rc = launched(launch_fill_u8(skip_bitmap, n, 0, st), "bitmap clear"))) return rc;
     }
-    return launched(launch_fmha_bf16(a, false, st), "dense attention");
+    return launched(launch_fmha_bf16(a, st), "dense attention");
   }
   a.log2_lambda = (float)std::log2((double)threshold_factor / (double)shape->S_kv);
   a.bitmap = skip_bitmap;
   a.counter = counter;
-  return launched(launch_fmha_bf16(a, true, st), "skip-softmax attention");
+  return launched(launch_fmha_bf16_skip(a, st), "skip-softmax attention");
 }
 
 int attn_sage_layout_query(const attn_shape* shape, const attn_recipe* recipe, attn_sage_layout* out) {

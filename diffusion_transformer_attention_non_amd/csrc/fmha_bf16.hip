@@ -1,20 +1,19 @@
-// Dense and Skip-Softmax BF16 attention for gfx950.
+// Dense BF16 attention for gfx950.
 //
 // Fused multi-head attention O = softmax(sm_scale * Q K^T) V, full context,
-// non-causal ("TRTLLM Attention", section "Dense mode"), with the optional
-// Skip-Softmax tile test ("TRTLLM Attention", section "Skip-Softmax"; the
-// threshold factor / seqlen of the knob table in "SAGE + Skip-Softmax - API
-// Design & Test Plan", Part 1 section 4).
+// non-causal ("TRTLLM Attention", section "Dense mode"; "Diffusion Attention
+// Backends", backend table: BF16, native GQA, head_dim 128).  The
+// Skip-Softmax variant is a separate kernel (fmha_skip.hip).
 //
 // Work decomposition
 //   workgroup = 4 wavefronts = 256 query rows of one (batch, query head);
 //   each wavefront owns 64 query rows and walks all KV tiles of 64 keys.
-//   Per tile and wavefront:
-//     BMM1  S^T[key, query] = K Q^T   32 x v_mfma_f32_32x32x16_bf16
+//   Per 32-key half of a tile and wavefront:
+//     BMM1  S^T[key, query] = K Q^T   16 x v_mfma_f32_32x32x16_bf16
 //           (A = K from LDS, B = Q kept in registers for the whole kernel);
 //     softmax on S^T: each lane holds one query column of each 32x32 block,
 //           so the row maximum is an in-lane max plus one v_permlane32_swap;
-//     BMM2  O^T[d, query] += V^T P^T   32 x v_mfma_f32_32x32x16_bf16
+//     BMM2  O^T[d, query] += V^T P^T   16 x v_mfma_f32_32x32x16_bf16
 //           (A = V^T read with ds_read_b64_tr_b16 from row-major V in LDS,
 //           B = P^T straight from the softmax registers).
 //   Computing the transposed products keeps each query in one lane, so the
@@ -24,26 +23,16 @@
 //   K/V tiles stream into a 4-stage LDS ring with buffer_load ... lds (no
 //   register staging; out-of-range rows read as zero), three tiles ahead; the
 //   loop is unrolled by the ring depth so every stage is a distinct array.
-//   The dense kernel splits each tile into two 32-key halves and runs four
-//   blocks per tile, each pairing MFMA work with independent VALU work:
-//     A: BMM1 (j, half 1)    || exponentials (j, half 0)
-//     B: BMM2 (j, half 0)    || row max (j, half 1), row sums (j, half 0)
-//     C: BMM1 (j+1, half 0)  || exponentials (j, half 1)
-//     D: BMM2 (j, half 1)    || row max (j+1, half 0), row sums (j, half 1)
-//   The order inside a block is written out (MFMA, its share of VALU work,
-//   scheduling fence), with LDS fragments read two MFMA steps ahead.
+//   Each half's VALU work rides on two 16-MFMA blocks (described with the
+//   blocks below); the order inside a block is written out (MFMA, its share
+//   of VALU work, scheduling fence), with LDS fragments read ahead.
 //
 // Online softmax with a lazy reference maximum: exponentials are taken
 // relative to a per-row reference m_ref (log2 units) that is raised only when
 // a tile's maximum exceeds it by more than 8, so P <= 2^8 and the O rescale
 // runs only when some row's maximum grows that much.  Softmax is invariant to
-// the reference, so the result is the same up to rounding.
-//
-// Skip-Softmax (kSkip): the KV tile of the vote is a 32-key half.  After its
-// BMM1, the wavefront skips the half (no exponentials, no BMM2) when every
-// valid row i of its 64 rows has exp(M_it - m_i) < lambda, M_it being the
-// row's maximum over the half and m_i the running maximum over the halves
-// kept so far; lambda = factor / S_kv.  The first half is always kept.
+// the reference, so the result is the same up to rounding.  Row sums add the
+// fp32 exponentials.
 #include <type_traits>
 
 #include "device_common.h"
@@ -52,6 +41,8 @@
 namespace ditattn {
 namespace {
 
+constexpr int kDenseWaveRows = 64;   // query rows per wavefront
+constexpr int kDenseWaves = kBlockM / kDenseWaveRows;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the reference max moves
@@ -99,8 +90,7 @@ __device__ __forceinline__ int key_of_mfma_row(int i) {
 //      physical chunk = logical chunk ^ (r & 7);
 //   V: row = key, physical chunk = logical chunk ^ (2 * (key & 3)).
 
-template <bool kSkip>
-__global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
+__global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sK2[kTileBytes];
@@ -130,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int q0 = qt * kBlockM + wave * kWaveRows;
+  const int q0 = qt * kBlockM + wave * kDenseWaveRows;
   const int Sq = p.Sq, Skv = p.Skv;
   const int nkt = (Skv + kBlockN - 1) / kBlockN;
 
@@ -203,98 +193,9 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
       for (int r = 0; r < 16; ++r) o[db][qb][r] = 0.0f;
 
   const float c = p.sm_scale * kLog2e;
-  float mref[2], mrun[2];
+  float mref[2];
   float lsum[2] = {0.0f, 0.0f};
-  const bool qvalid0 = q0 + l32 < Sq, qvalid1 = q0 + 32 + l32 < Sq;
-  unsigned skipped = 0;
-  const int nqb = (Sq + kWaveRows - 1) / kWaveRows;
-  const int nvote = (Skv + kSkipBlockN - 1) / kSkipBlockN;
-  uint8_t* bitmap_row = nullptr;
-  if (kSkip && p.bitmap != nullptr && q0 < Sq)
-    bitmap_row = p.bitmap + ((int64_t)(b * p.Hq + h) * nqb + q0 / kWaveRows) * nvote;
 
-  f32x16 s0[2], s1[2];   // S^T of the tile's two 32-key halves, [qb]
-  bf16x8 pf[2][2][2];    // P^T of the tile, [half][16-key step][qb]
-
-  // BMM1 of one 32-key half from K stage ks (16 MFMAs, 8 LDS reads).
-  auto bmm1 = [&](const uint8_t* ks, int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = 0.0f;
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + ka[ds & 3] + kb * 32 * kRowBytes + 128 * (ds >> 2));
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ds], s[qb], 0, 0, 0);
-    }
-  };
-  // P = exp2(s * c - m_ref) of one half, packed to bf16.
-  auto softmax_exp = [&](f32x16 (&s)[2], int half) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float nb = -mref[qb];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        f32x8 e;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = exp2_fast(__builtin_fmaf(s[qb][8 * s2 + j], c, nb));
-        pf[half][s2][qb] = __builtin_convertvector(e, bf16x8);
-      }
-    }
-  };
-  // BMM2 of one half: O^T += V^T P^T (16 MFMAs, 16 transposing LDS reads).
-  auto bmm2 = [&](const uint8_t* vs, int half) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int off = (32 * half + 16 * s2) * kRowBytes + 128 * (db >> 1);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off));
-        const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off + 4 * kRowBytes));
-        const bf16x8 a = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[half][s2][qb], o[db][qb], 0, 0, 0);
-      }
-  };
-  // Row sums of the packed P of one half (the values BMM2 multiplies).
-  auto rowsum = [&](int half) __attribute__((always_inline)) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float acc = lsum[qb];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc = __builtin_amdgcn_fdot2_f32_bf16(bf16_pair(pf[half][s2][qb], j), ones, acc, false);
-      lsum[qb] = acc;
-    }
-  };
-  // Half-tile maximum per query in log2 units; keys past S_kv are masked first.
-  auto rowmax = [&](f32x16 (&s)[2], int key0, float (&mx)[2]) __attribute__((always_inline)) {
-    if (key0 + 32 > Skv) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 16 * (r >> 3) + 8 * hh + (r & 7);
-        if (key >= Skv) {
-          s[0][r] = kNegInf;
-          s[1][r] = kNegInf;
-        }
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float m = s[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) m = fmaxf(m, s[qb][r]);
-      mx[qb] = max_halves(m) * c;
-    }
-  };
   // ---- Dense pipeline.  A half-tile (32 keys) goes through BMM1 (S), the row
   // maximum, 16 exponential pairs (P) and BMM2.  Two 16-MFMA blocks per half
   // carry its VALU work:
@@ -460,26 +361,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
         for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
     }
   };
-  // Skip vote for half-tile u (u > 0): kept unless every valid row is below lambda.
-  auto decide = [&](const float (&mx)[2], int u) __attribute__((always_inline)) -> bool {
-    bool keep = true;
-    if (u > 0) {
-      const bool need = (qvalid0 && !(mx[0] - mrun[0] < p.log2_lambda)) ||
-                        (qvalid1 && !(mx[1] - mrun[1] < p.log2_lambda));
-      keep = __any(need);
-    }
-    if (keep) {
-      mrun[0] = fmaxf(mrun[0], mx[0]);
-      mrun[1] = fmaxf(mrun[1], mx[1]);
-    } else {
-      ++skipped;
-    }
-    if (bitmap_row != nullptr && lane == 0) bitmap_row[u] = keep ? 0 : 1;
-    return keep;
-  };
-
   mref[0] = mref[1] = kNegInf;
-  mrun[0] = mrun[1] = kNegInf;
 
   // ---- Prologue: tiles 0..2 in flight.
   issue_loads(IC<0>{}, 0);
@@ -497,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
       redo_q_pairs(sv, pout);
     }
   };
-  if constexpr (!kSkip) {
+  if constexpr (true) {
     // S of half 0 (tile 0), then its Q-block VALU work with no BMM2 to pair with.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));
     wg_barrier();
@@ -521,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     const uint8_t* ks = kst(IC<S>{});
     const uint8_t* vs = vst(IC<S>{});
     const int key0 = j * kBlockN;
-    if constexpr (!kSkip) {
+    if constexpr (true) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));   // tile j+1 landed (j+2 may be in flight)
       wg_barrier();
       // Tile j+3 goes into the stage tile j-1 used (every wavefront is past
@@ -545,30 +427,6 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
       mask_half(sb[0], key0 + kBlockN);
       bmm2_block(vs, 1, pb[1], [&](int t) __attribute__((always_inline)) { q_valu(sb[0], pb[0], t); });
       q_check(sb[0], pb[0]);
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));   // tile j landed (j+1, j+2 may be in flight)
-      wg_barrier();
-      issue_loads(IC<(S + 3) & 3>{}, j + 3);
-      // Skip-Softmax: each 32-key half is a KV tile of its own for the vote.
-      bmm1(ks, 0, s0);
-      rowmax(s0, key0, mx0);
-      const bool keep0 = decide(mx0, 2 * j);
-      if (keep0) {
-        if (needs_rescale(mx0)) rescale(mx0);
-        softmax_exp(s0, 0);
-      }
-      bmm1(ks, 1, s1);
-      rowmax(s1, key0 + 32, mx1);
-      if (keep0) {
-        bmm2(vs, 0);
-        rowsum(0);
-      }
-      if (key0 + 32 < Skv && decide(mx1, 2 * j + 1)) {
-        if (needs_rescale(mx1)) rescale(mx1);
-        softmax_exp(s1, 1);
-        bmm2(vs, 1);
-        rowsum(1);
-      }
     }
   };
 
@@ -583,9 +441,6 @@ __global__ __launch_bounds__(256, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
     if (j + 4 >= nkt) break;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-
-  if (kSkip && p.counter != nullptr && lane == 0 && q0 < Sq && skipped)
-    atomicAdd(p.counter, (unsigned long long)skipped);
 
   // ---- Epilogue: O = O^T / l, lane writes 4 consecutive d per register group.
 #pragma unroll
@@ -625,14 +480,11 @@ __global__ void fill_u8_kernel(uint8_t* p, size_t n, uint8_t value) {
 
 }  // namespace
 
-hipError_t launch_fmha_bf16(const FmhaBf16Args& a, bool skip, hipStream_t stream) {
+hipError_t launch_fmha_bf16(const FmhaBf16Args& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
   const int64_t nwg = nqt * a.Hq * a.B;
   if (nwg <= 0) return hipSuccess;
-  if (skip)
-    hipLaunchKernelGGL(fmha_bf16_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(fmha_bf16_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(fmha_bf16_kernel, dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -39,8 +39,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kSageWaves = 8;
-constexpr int kSageWaveRows = kBlockM / kSageWaves;   // 32 query rows per wavefront
+constexpr int kSageWaves = kWavesPerWG;
+constexpr int kSageWaveRows = kWaveRows;   // 32 query rows per wavefront
 constexpr int kKTileB = kBlockN * kHeadDim;   // 8 KB of K codes
 constexpr int kVTileB = kHeadDim * kBlockN;   // 8 KB of V^T codes
 constexpr int kScaleOff = kKTileB + kVTileB;  // 64 fp32 K scales follow

@@ -8,8 +8,9 @@ namespace ditattn {
 
 // Tile geometry shared by the attention kernels and the host layer.
 constexpr int kHeadDim = 128;
-constexpr int kWaveRows = 64;    // query rows owned by one wavefront (skip decision unit)
-constexpr int kWavesPerWG = 4;
+constexpr int kWaveRows = 32;    // query rows per wavefront in the SAGE and Skip-Softmax kernels
+                                  // (the Skip-Softmax decision unit)
+constexpr int kWavesPerWG = 8;   // two wavefronts per SIMD
 constexpr int kBlockM = kWaveRows * kWavesPerWG;  // query rows per workgroup
 constexpr int kBlockN = 64;       // keys per KV tile (LDS stage)
 constexpr int kSkipBlockN = 32;   // keys per Skip-Softmax vote (half a KV tile)
@@ -29,7 +30,8 @@ struct FmhaBf16Args {
   unsigned long long* counter;      // nullable
 };
 
-hipError_t launch_fmha_bf16(const FmhaBf16Args& a, bool skip, hipStream_t stream);
+hipError_t launch_fmha_bf16(const FmhaBf16Args& a, hipStream_t stream);        // dense
+hipError_t launch_fmha_bf16_skip(const FmhaBf16Args& a, hipStream_t stream);   // Skip-Softmax
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
 hipError_t launch_fill_u8(uint8_t* p, size_t n, uint8_t value, hipStream_t stream);
 

@@ -153,7 +153,7 @@ int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o
 /* Skip-Softmax attention on BF16 ([TA] "Skip-Softmax"; [SSD] knob table:
  * skip_softmax_threshold_scale_factor, threshold = factor / seqlen).
  *   lambda = threshold_factor / S_kv.  Queries are tiled in blocks of
- *   block_m rows and keys in tiles of block_n keys (attn_tile_config: 64
+ *   block_m rows and keys in tiles of block_n keys (attn_tile_config: 32
  *   rows x 32 keys).  For
  *   each query block, KV tiles are visited in ascending order; tile t > 0 is
  *   skipped when, for every valid row i of the block,
