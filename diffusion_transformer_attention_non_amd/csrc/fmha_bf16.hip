@@ -83,12 +83,11 @@ __device__ __forceinline__ int key_of_mfma_row(int i) {
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
-// LDS tile layouts (16-byte chunks, 16 per 256-byte row, XOR-swizzled so that
-// every read phase hits distinct banks and every read address is a lane
-// constant plus an immediate):
+// LDS tile layouts (256-byte rows, swizzled so that the lanes one LDS cycle
+// serves hit 64 distinct four-byte banks):
 //   K: row r = MFMA row (32*(r/32) + key_of_mfma_row(r%32) is the key),
-//      physical chunk = logical chunk ^ (r & 7);
-//   V: row = key, physical chunk = logical chunk ^ (2 * (key & 3)).
+//      physical 16-byte chunk = logical chunk ^ (r & 15);
+//   V: row = key, physical 64-byte segment = logical segment ^ (key & 3).
 
 __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTileBytes];
@@ -156,8 +155,8 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     const int r = 16 * i + 4 * wave + (lane >> 4);
     const int pch = lane & 15;
     const int kkey = 32 * (r >> 5) + key_of_mfma_row(r & 31);
-    koff[i] = (uint32_t)kkey * kstride + 16u * (uint32_t)(pch ^ (r & 7));
-    voff[i] = (uint32_t)r * vstride + 16u * (uint32_t)(pch ^ (2 * (r & 3)));
+    koff[i] = (uint32_t)kkey * kstride + 16u * (uint32_t)(pch ^ (r & 15));
+    voff[i] = (uint32_t)r * vstride + 64u * (uint32_t)((pch >> 2) ^ (r & 3)) + 16u * (uint32_t)(pch & 3);
   }
   const uint32_t wave_slot = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * wave);
   auto issue_loads = [&](auto s, int t) __attribute__((always_inline)) {
@@ -171,17 +170,20 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   };
 
   // ---- LDS read addresses (lane constants; the rest is immediate).
-  int ka[4], va[2];
+  //   K fragment (kb, ds): row 32 kb + l32, logical chunk 2 ds + hh.
+  //   V^T fragment (db, 4 keys from key k0 + 8 hh, k0 a multiple of 4), read
+  //   with ds_read_b64_tr_b16: lane x of each 16-lane group addresses key
+  //   k0 + 8 hh + (x%16)/4, channels 32 db + 16 ((x/16) % 2) + 4 (x%4) + 0..3;
+  //   the transposing read hands lane 16 G + 4 a + j channel 32 db + 16 (G%2)
+  //   + 4 a + j of the four keys.
+  int ka[8], va[4];
   {
-    const int f = l32 & 7;
+    const int f = l32 & 15;
 #pragma unroll
-    for (int dl = 0; dl < 4; ++dl) ka[dl] = l32 * kRowBytes + 16 * (hh ^ (f & 1)) + 32 * (dl ^ (f >> 1));
-    const int r16 = lane & 15, gq = lane >> 4;
-    const int x = 2 * (gq & 1) + ((r16 & 3) >> 1);
-    const int y = 2 * (r16 >> 2);
+    for (int ds = 0; ds < 8; ++ds) ka[ds] = l32 * kRowBytes + 16 * ((2 * ds + hh) ^ f);
+    const int i = (lane & 15) >> 2, a = lane & 3, gg = (lane >> 4) & 1;
 #pragma unroll
-    for (int dl = 0; dl < 2; ++dl)
-      va[dl] = (8 * hh + (r16 >> 2)) * kRowBytes + 64 * (dl ^ (y >> 2)) + 16 * (x ^ (y & 3)) + 8 * (r16 & 1);
+    for (int db = 0; db < 4; ++db) va[db] = (8 * hh + i) * kRowBytes + 64 * (db ^ i) + 32 * gg + 8 * a;
   }
 
   f32x16 o[4][2];
@@ -208,14 +210,14 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   // and add to the row sum), so no slot waits on its own results.
   auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
   auto kfrag = [&](const uint8_t* ks, int kb, int ds) __attribute__((always_inline)) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(ks + ka[ds & 3] + kb * 32 * kRowBytes + 128 * (ds >> 2));
+    return *reinterpret_cast<const bf16x8*>(ks + ka[ds] + kb * 32 * kRowBytes);
   };
   auto vfrag = [&](const uint8_t* vs, int half, int step) __attribute__((always_inline)) -> bf16x8 {
     const int s2 = step >> 2, db = step & 3;
-    const int off = (32 * half + 16 * s2) * kRowBytes + 128 * (db >> 1);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off));
+    const int off = (32 * half + 16 * s2) * kRowBytes;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db] + off));
     const s16x4 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db & 1] + off + 4 * kRowBytes));
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((DITATTN_LDS s16x4*)(vs + va[db] + off + 4 * kRowBytes));
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4,
                                    5, 6, 7);
   };
