@@ -107,8 +107,9 @@ typedef struct {
 /* Dense BF16 attention ([TA] "Dense mode"; [DAB] backend table).
  *   O = softmax(sm_scale * Q K^T) V, per batch entry and query head.
  *   q, k, v: device bf16 per the layout above; o: device, o_dtype BF16 or
- *   FP32 (round to nearest even).  sm_scale: any finite float (typically
- *   1/sqrt(128)).  Errors: INVALID_ARG, UNSUPPORTED_HEAD_DIM, BAD_GQA,
+ *   FP32 (round to nearest even).  sm_scale: finite and > 0 (typically
+ *   1/sqrt(128); INVALID_ARG otherwise).  Errors: INVALID_ARG,
+ *   UNSUPPORTED_HEAD_DIM, BAD_GQA,
  *   BAD_LAYOUT, DEVICE.  Empty problems (B, S_q, Hq = 0) return OK with no
  *   launch; S_kv = 0 with S_q > 0 is INVALID_ARG (softmax over no keys). */
 int attn_dense_bf16(const void* q, const void* k, const void* v, void* o,
