@@ -25,10 +25,11 @@ Parity status per function is listed in each module's header.
 from .codecs import (bf16_round, e4m3_decode, e4m3_encode, f32, int8_code,
                      E4M3_MAX, INT8_MAX)
 from .attention import (exact_attention, sage_quantize, sage_attention,
-                        skip_attention, skip_gate_enabled, k_channel_mean)
+                        sage_skip_attention, skip_attention, skip_gate_enabled,
+                        k_channel_mean)
 
 __all__ = [
     "bf16_round", "e4m3_decode", "e4m3_encode", "f32", "int8_code", "E4M3_MAX",
-    "INT8_MAX", "exact_attention", "sage_quantize", "sage_attention",
+    "INT8_MAX", "exact_attention", "sage_quantize", "sage_attention", "sage_skip_attention",
     "skip_attention", "skip_gate_enabled", "k_channel_mean",
 ]

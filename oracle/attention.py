@@ -21,6 +21,11 @@ Parity status:
   sage_attention    pinned: Q = 0 closed form, equality with exact attention
                     on exactly representable inputs with P rounding off,
                     independence of the KV tile size with P rounding off.
+  sage_skip_attention pinned: factor 0 equals sage_attention bit for bit;
+                    with P rounding off, skip set and output equal
+                    skip_attention on the dequantized inputs; monotone in the
+                    factor; first tile never skipped; a dominant first tile
+                    skips every later one.
   skip_attention    pinned: factor 0 equals exact attention, monotone skip
                     sets, first tile never skipped, scalar brute force on tiny
                     grids, dropped-mass error bound, a constructed case where
@@ -281,6 +286,86 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
                     m = m2
                 out[b, :, h, :] = acc * sv[None, :] / l[:, None]
     return _round_out(out, out_dtype)
+
+
+def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, quantize_p=True,
+                        p_scale=256.0, out_dtype=None):
+    """SAGE attention with the Skip-Softmax tile test, emulated in float64.
+
+    Both options in one pass ("Diffusion Attention Backends" and "TRTLLM
+    Attention": Skip-Softmax runs on the same TRTLLM backend as SAGE;
+    "VisualGen Quantized Attention", section "Interaction With Other
+    Features": the two are exercised together; "SAGE + Skip-Softmax - API
+    Design & Test Plan", Part 1 section 4 for threshold = factor / seqlen).
+    Readings taken:
+      * the skip test runs on the dequantized logits of the SAGE path,
+        L_ij = log2(e) * sm_scale * sq(i) * sk(j) * <qc_i, kc_j> (log2 units,
+        so exp(M - m) < lambda reads 2**(M_L - m_L) < lambda);
+      * queries in tiles of ``block_m`` rows, keys in the KV tiles of
+        ``block_n`` keys of the SAGE online softmax; tile t > 0 of a query
+        tile is skipped iff every valid row i has 2**(M_it - m_i) < lambda =
+        factor / S_kv, M_it the row's largest L in the tile and m_i its exact
+        running maximum over the kept tiles (not the integer reference);
+      * a skipped tile changes nothing: not m, not the SAGE reference, not the
+        row sum, not the accumulator;
+      * every kept tile is processed exactly as in ``sage_attention``.
+    ``qtiles`` selects query tiles (default: all).  Returns (O [B, R, Hq, D],
+    skipped [B, Hq, nQT, T] bool, ratio [B, Hq, nQT, T] = max_i
+    2**(M_it - m_i) with NaN at t = 0, rows).
+    """
+    dt = quant["qk_dtype"]
+    qb, kb = quant["q_block"], quant["k_block"]
+    qc_all, kc_all, vc_all = quant["q_codes"], quant["k_codes"], quant["v_codes"]
+    B, Hq, Sq, D = qc_all.shape
+    Hkv, Skv = kc_all.shape[1], kc_all.shape[2]
+    G = Hq // Hkv
+    nqt = -(-Sq // block_m)
+    T = -(-Skv // block_n)
+    qtiles = np.arange(nqt) if qtiles is None else np.asarray(qtiles)
+    lam = float(factor) / Skv
+    log2_lam = math.log2(lam) if lam > 0 else -math.inf
+    rows = np.concatenate([np.arange(t * block_m, min(Sq, (t + 1) * block_m)) for t in qtiles])
+    out = np.empty((B, len(rows), Hq, D))
+    skipped = np.zeros((B, Hq, len(qtiles), T), bool)
+    ratio = np.full((B, Hq, len(qtiles), T), np.nan)
+    keys = np.arange(Skv)
+    for b in range(B):
+        for g in range(Hkv):
+            kc = _decode(kc_all[b, g], dt)
+            sk = quant["k_scale"][b, g][keys // kb].astype(np.float64)
+            vd = e4m3_decode(vc_all[b, g])
+            sv = quant["v_scale"][b, g].astype(np.float64)
+            for h in range(g * G, (g + 1) * G):
+                r0 = 0
+                for qi, qt in enumerate(qtiles):
+                    rr = np.arange(qt * block_m, min(Sq, (qt + 1) * block_m))
+                    qc = _decode(qc_all[b, h][rr], dt)
+                    sq = quant["q_scale"][b, h][rr // qb].astype(np.float64)
+                    s = sm_scale * sq[:, None] * sk[None, :] * (qc @ kc.T) * LOG2E
+                    m_true = np.full(len(rr), -np.inf)
+                    m = np.full(len(rr), -np.inf)
+                    l = np.zeros(len(rr))
+                    acc = np.zeros((len(rr), D))
+                    for t in range(T):
+                        st = s[:, t * block_n:(t + 1) * block_n]
+                        mt = st.max(axis=1)
+                        if t > 0:
+                            gap = mt - m_true
+                            ratio[b, h, qi, t] = 2.0 ** gap.max()
+                            if np.all(gap < log2_lam):
+                                skipped[b, h, qi, t] = True
+                                continue
+                        m_true = np.maximum(m_true, mt)
+                        m2 = np.maximum(m, np.ceil(mt))
+                        alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - m2))
+                        p = np.exp2(st - m2[:, None])
+                        pq = e4m3_decode(e4m3_encode(p_scale * p)) if quantize_p else p_scale * p
+                        l = alpha * l + pq.sum(axis=1)
+                        acc = alpha[:, None] * acc + pq @ vd[t * block_n:(t + 1) * block_n]
+                        m = m2
+                    out[b, r0:r0 + len(rr), h, :] = acc * sv[None, :] / l[:, None]
+                    r0 += len(rr)
+    return _round_out(out, out_dtype), skipped, ratio, rows
 
 
 # ----------------------------------------------------------------------------
