@@ -88,10 +88,24 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
 // another.  With both operands equal to x, the first result holds x[l % 32]
 // and the second x[32 + l % 32] in every lane l, so combining them reduces
 // over the two wave halves (lanes l and l ^ 32).
+// Maxima as single v_max / v_max3 instructions.  fmaxf would first quiet
+// signalling NaNs (an extra canonicalizing v_max per operand that is not
+// known to be canonical); no NaN reaches these maxima.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float max_halves(float x) {
   const unsigned u = __float_as_uint(x);
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_halves(float x) {

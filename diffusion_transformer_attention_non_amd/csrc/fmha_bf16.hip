@@ -31,8 +31,8 @@
 // relative to a per-row reference m_ref (log2 units) that is raised only when
 // a tile's maximum exceeds it by more than 8, so P <= 2^8 and the O rescale
 // runs only when some row's maximum grows that much.  Softmax is invariant to
-// the reference, so the result is the same up to rounding.  Row sums add the
-// fp32 exponentials.
+// the reference, so the result is the same up to rounding.  Row sums are taken
+// on the matrix cores from the bf16 P that BMM2 multiplies.
 #include <type_traits>
 
 #include "device_common.h"
@@ -196,7 +196,25 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
 
   const float c = p.sm_scale * kLog2e;
   float mref[2];
-  float lsum[2] = {0.0f, 0.0f};
+  // Row sums of P on the matrix cores: v_mfma_f32_16x16x32_bf16 with B = the
+  // BMM2 operand P^T (lane l: query 32 qb + l % 32, 8 keys from 8 (l / 32))
+  // and a 0/1 selector A whose row 0 takes lane groups 0 and 2 (queries
+  // 32 qb + 0..15) and row 1 groups 1 and 3 (queries 32 qb + 16..31).  Result
+  // register r of lane n < 16 then holds the row sum of query 32 qb + 16 r + n
+  // (r = 0, 1); every other entry stays zero.  The sums are of the bf16 P that
+  // BMM2 multiplies.
+  bf16x8 rsel;
+  {
+    const int m = lane & 15, grp = lane >> 4;
+    const __bf16 one = (m < 2 && m == (grp & 1)) ? (__bf16)1.0f : (__bf16)0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rsel[i] = one;
+  }
+  f32x4 rsum[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rsum[qb][r] = 0.0f;
 
   // ---- Dense pipeline.  A half-tile (32 keys) goes through BMM1 (S), the row
   // maximum, 16 exponential pairs (P) and BMM2.  Two 16-MFMA blocks per half
@@ -206,8 +224,8 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   // The exponentials of the Q block are taken with the reference maximum as
   // it stands (speculatively); the check after the block redoes them in the
   // rare case the reference has to move.  Every pair runs a three-stage
-  // pipeline over consecutive MFMA slots (scale and shift, exp2, pack to bf16
-  // and add to the row sum), so no slot waits on its own results.
+  // pipeline over consecutive MFMA slots (scale and shift, exp2, pack to
+  // bf16), so no slot waits on its own results.
   auto fence = [&]() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
   auto kfrag = [&](const uint8_t* ks, int kb, int ds) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(ks + ka[ds] + kb * 32 * kRowBytes);
@@ -253,6 +271,10 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       const int s2 = step >> 2, db = step & 3;
       if (qb == 0 && step + kPrefetch < 8) vfr[(step + kPrefetch) % (kPrefetch + 1)] = vfrag(vs, half, step + kPrefetch);
       o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[step % (kPrefetch + 1)], pin[s2][qb], o[db][qb], 0, 0, 0);
+      if ((t & 3) == 3) {
+        const int rq = (t >> 2) & 1, rs = t >> 3;
+        rsum[rq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, pin[rs][rq], rsum[rq], 0, 0, 0);
+      }
       valu(t);
       fence();
     }
@@ -260,7 +282,6 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   // Exponential pipeline, pair k (0..15) of a half: qb = k / 8, 16-key step
   // s2 = (k / 4) % 2, register pair k % 4 of that step.
   float ex[3][2];       // pairs in flight, slot k % 3
-  float lp[2][2];       // partial row sums of the half in flight, [qb][even/odd key]
   auto pair_stage = [&](int stage, const f32x16 (&sv)[2], bf16x8 (&pout)[2][2], int k) __attribute__((always_inline)) {
     const int qb = k >> 3, s2 = (k >> 2) & 1, jp = k & 3;
     float(&x)[2] = ex[k % 3];
@@ -273,12 +294,10 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       x[1] = exp2_fast(x[1]);
       asm volatile("" : "+v"(x[0]), "+v"(x[1]));
     } else {
-      lp[qb][0] += x[0];
-      lp[qb][1] += x[1];
       i32x4 w = __builtin_bit_cast(i32x4, pout[s2][qb]);
       const bf16x2 pr = {(__bf16)x[0], (__bf16)x[1]};
       int word = __builtin_bit_cast(int, pr);
-      asm volatile("" : "+v"(word), "+v"(lp[qb][0]), "+v"(lp[qb][1]));
+      asm volatile("" : "+v"(word));
       w[jp] = word;
       pout[s2][qb] = __builtin_bit_cast(bf16x8, w);
     }
@@ -288,18 +307,15 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   auto max_stage = [&](const f32x16 (&sv)[2], int i) __attribute__((always_inline)) {
     const int qb = i >> 3, r = i & 7;
     if (r == 0)
-      mpart[qb] = fmaxf(fmaxf(sv[qb][0], sv[qb][1]), sv[qb][2]);
+      mpart[qb] = max3_raw(sv[qb][0], sv[qb][1], sv[qb][2]);
     else if (r < 7)
-      mpart[qb] = fmaxf(fmaxf(mpart[qb], sv[qb][2 * r + 1]), sv[qb][2 * r + 2]);
+      mpart[qb] = max3_raw(mpart[qb], sv[qb][2 * r + 1], sv[qb][2 * r + 2]);
     else
-      mpart[qb] = fmaxf(mpart[qb], sv[qb][15]);
+      mpart[qb] = max_raw(mpart[qb], sv[qb][15]);
   };
   // VALU work of a Q block: max step t, and pairs 0..6 at slots 2k (fma), 2k+1 (exp), 2k+2 (pack).
   auto q_valu = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2], int t) __attribute__((always_inline)) {
     max_stage(sv, t);
-    if (t == 0) {
-      lp[0][0] = lp[0][1] = lp[1][0] = lp[1][1] = 0.0f;
-    }
     if ((t & 1) == 0 && t >= 2) pair_stage(2, sv, pout, (t - 2) >> 1);
     if ((t & 1) == 1) pair_stage(1, sv, pout, (t - 1) >> 1);
     if ((t & 1) == 0 && t <= 12) pair_stage(0, sv, pout, t >> 1);
@@ -322,17 +338,12 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   // Slow path after a Q block whose maximum moved the reference: rescale the
   // running state, then redo pairs 0..6 with the new reference.
   auto redo_q_pairs = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2]) __attribute__((always_inline)) {
-    lp[0][0] = lp[0][1] = lp[1][0] = lp[1][1] = 0.0f;
 #pragma unroll
     for (int k = 0; k < 7; ++k) {
       pair_stage(0, sv, pout, k);
       pair_stage(1, sv, pout, k);
       pair_stage(2, sv, pout, k);
     }
-  };
-  auto add_row_sums = [&]() __attribute__((always_inline)) {
-    lsum[0] += lp[0][0] + lp[0][1];
-    lsum[1] += lp[1][0] + lp[1][1];
   };
   // Tail mask of a half starting at key key0 (keys past S_kv take no part).
   auto mask_half = [&](f32x16 (&s)[2], int key0) __attribute__((always_inline)) {
@@ -356,7 +367,9 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       const float mnew = fmaxf(mref[qb], mx[qb]);
       const float alpha = exp2_fast(mref[qb] - mnew);
       mref[qb] = mnew;
-      lsum[qb] *= alpha;
+      const float alpha_hi = __shfl(alpha, (lane & 15) + 16, 64);
+      rsum[qb][0] *= alpha;
+      rsum[qb][1] *= alpha_hi;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -417,7 +430,6 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
         p_valu(sb[0], pb[0], t);
         if ((t & 3) == 2) buffer_load_lds16(krsrc, kd + 4096 * (t >> 2), koff[t >> 2] + tk);
       });
-      add_row_sums();
       mask_half(sb[1], key0 + 32);
       bmm2_block(vs, 0, pb[0], [&](int t) __attribute__((always_inline)) {
         q_valu(sb[1], pb[1], t);
@@ -425,7 +437,6 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       });
       q_check(sb[1], pb[1]);
       bmm1_block(kst(IC<(S + 1) & 3>{}), 0, sb[0], [&](int t) __attribute__((always_inline)) { p_valu(sb[1], pb[1], t); });
-      add_row_sums();
       mask_half(sb[0], key0 + kBlockN);
       bmm2_block(vs, 1, pb[1], [&](int t) __attribute__((always_inline)) { q_valu(sb[0], pb[0], t); });
       q_check(sb[0], pb[0]);
@@ -447,8 +458,8 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   // ---- Epilogue: O = O^T / l, lane writes 4 consecutive d per register group.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l = sum_halves(lsum[qb]);
-    const float inv = 1.0f / l;
+    const float s_lo = __shfl(rsum[qb][0], l32 & 15, 64), s_hi = __shfl(rsum[qb][1], l32 & 15, 64);
+    const float inv = 1.0f / (l32 < 16 ? s_lo : s_hi);
     const int row = q0 + qb * 32 + l32;
     if (row < Sq) {
       const int64_t obase = b * p.os[0] + (int64_t)row * p.os[1] + h * p.os[2];
