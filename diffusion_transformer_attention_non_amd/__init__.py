@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   sage_quantize(q, k, v, recipe)           SAGE codes and scales
   attn_sage(q, k, v, recipe)               SAGE attention
   attn_skip_softmax(q, k, v, factor)       Skip-Softmax attention
+  attn_sage_skip_softmax(q, k, v, recipe, factor)   SAGE with Skip-Softmax
   SkipGate(D).enabled(t)                   host-side timestep gate
   attention(...)                           one call that routes a DiT layer
 
@@ -29,7 +30,8 @@ import torch
 
 __all__ = [
     "AttnError", "SageRecipe", "SkipGate", "attn_dense_bf16", "sage_quantize",
-    "attn_sage", "attn_skip_softmax", "attention", "tile_config", "library_path",
+    "attn_sage", "attn_skip_softmax", "attn_sage_skip_softmax", "attention", "tile_config",
+    "kv_tile", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +93,7 @@ def _lib():
             "sage_quantize": [P, P, P, SP, RP, P, ctypes.c_size_t, P],
             "attn_sage": [P, P, P, P, I, SP, RP, F, P, ctypes.c_size_t, P],
             "attn_skip_softmax": [P, P, P, P, I, SP, F, F, P, P, P],
+            "attn_sage_skip_softmax": [P, P, P, P, I, SP, RP, F, F, P, P, P, ctypes.c_size_t, P],
             "attn_skip_gate": [F, F, ctypes.POINTER(I)],
             "attn_tile_config": [ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
             "attn_version": [],
@@ -320,6 +323,44 @@ def attn_skip_softmax(q, k, v, threshold_factor, out=None, out_dtype=torch.bfloa
     return out, extras
 
 
+def attn_sage_skip_softmax(q, k, v, recipe: SageRecipe, threshold_factor, out=None, out_dtype=torch.bfloat16,
+                           sm_scale=None, workspace=None, return_bitmap=False, return_count=False):
+    """SAGE attention with the Skip-Softmax tile test (threshold_factor / S_kv)
+    on its dequantized logits, in one kernel.
+
+    The vote tile is block_m query rows x one KV tile (``tile_config()[0]`` x
+    ``kv_tile()``).  Returns out, or (out, extras) as attn_skip_softmax.
+    """
+    _check_tensors(q, k, v)
+    out, odt = _out(q, out, out_dtype)
+    lay = _layout(q, k, v, recipe)
+    if workspace is None:
+        workspace = torch.empty(max(1, lay.total_bytes), dtype=torch.uint8, device=q.device)
+    shape = _shape(q, k, v, out)
+    bm, _ = tile_config()
+    kv = kv_tile()
+    bitmap = cnt = None
+    if return_bitmap:
+        B, Sq, Hq, _ = q.shape
+        bitmap = torch.empty((B, Hq, -(-Sq // bm), -(-k.shape[1] // kv)), dtype=torch.uint8, device=q.device)
+    if return_count:
+        cnt = torch.empty(1, dtype=torch.int64, device=q.device)
+    _check(_lib().attn_sage_skip_softmax(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), odt,
+                                         ctypes.byref(shape), ctypes.byref(recipe._c()), _scale(q, sm_scale),
+                                         float(threshold_factor),
+                                         bitmap.data_ptr() if bitmap is not None else None,
+                                         cnt.data_ptr() if cnt is not None else None,
+                                         workspace.data_ptr(), workspace.numel(), _stream(q)))
+    if not (return_bitmap or return_count):
+        return out
+    extras = {}
+    if bitmap is not None:
+        extras["bitmap"] = bitmap
+    if cnt is not None:
+        extras["skipped"] = cnt
+    return out, extras
+
+
 class SkipGate:
     """Host-side gate: Skip-Softmax runs on a step iff its normalized timestep t <= D.
 
@@ -340,10 +381,10 @@ class SkipGate:
 def attention(q, k, v, *, quant: SageRecipe | None = None, skip_threshold: float | None = None,
               gate: SkipGate | None = None, timestep: float | None = None, attn_mask=None,
               out=None, out_dtype=torch.bfloat16, sm_scale=None):
-    """One DiT attention call: dense, SAGE, or Skip-Softmax when the gate allows.
+    """One DiT attention call: dense, SAGE, Skip-Softmax (when the gate
+    allows), or SAGE with Skip-Softmax.
 
-    A mask is refused: this backend only serves mask-free layers.  SAGE and
-    Skip-Softmax together are not offered by the kernels yet.
+    A mask is refused: this backend only serves mask-free layers.
     """
     if attn_mask is not None:
         raise ValueError("attention masks are not supported: this path is mask-free only")
@@ -353,7 +394,8 @@ def attention(q, k, v, *, quant: SageRecipe | None = None, skip_threshold: float
             raise ValueError("a gated Skip-Softmax call needs the normalized timestep")
         use_skip = gate.enabled(timestep)
     if quant is not None and use_skip:
-        raise ValueError("SAGE together with Skip-Softmax is not available")
+        return attn_sage_skip_softmax(q, k, v, quant, skip_threshold, out=out, out_dtype=out_dtype,
+                                      sm_scale=sm_scale)
     if quant is not None:
         return attn_sage(q, k, v, quant, out=out, out_dtype=out_dtype, sm_scale=sm_scale)
     if use_skip:

@@ -254,6 +254,68 @@ SageQuantArgs quant_args(const void* q, const void* k, const void* v, const attn
   return a;
 }
 
+// SAGE attention, with the Skip-Softmax tile test when threshold_factor > 0:
+// quantize into ws, then one attention launch.
+int run_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype, const attn_shape* shape,
+             const attn_recipe* recipe, float sm_scale, float threshold_factor, uint8_t* skip_bitmap,
+             uint64_t* skipped_tiles, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
+  if (rc) return rc;
+  attn_sage_layout L;
+  if ((rc = check_recipe(recipe))) return rc;
+  if (empty(shape)) return ok();
+  if ((rc = check_sage(q, k, v, shape, recipe, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_ptrs(q, k, v, o))) return rc;
+  if ((rc = check_device_ptr(ws, "workspace"))) return rc;
+  if (skip_bitmap && (rc = check_device_ptr(skip_bitmap, "skip_bitmap"))) return rc;
+  if (skipped_tiles) {
+    if ((reinterpret_cast<uintptr_t>(skipped_tiles) & 7u) != 0)
+      return fail(ATTN_ERR_BAD_LAYOUT, "skipped_tiles must be 8-byte aligned");
+    if ((rc = check_device_ptr(skipped_tiles, "skipped_tiles"))) return rc;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SageQuantArgs qa = quant_args(q, k, v, shape, recipe, ws, L);
+  if ((rc = launched(launch_sage_quantize(qa, st), "SAGE quantization"))) return rc;
+  FmhaSageArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q_codes = qa.q_codes;
+  a.k_codes = qa.k_codes;
+  a.v_codes = qa.v_codes;
+  a.q_scale = qa.q_scale;
+  a.k_scale = qa.k_scale;
+  a.v_scale = qa.v_scale;
+  a.o = o;
+  for (int i = 0; i < 3; ++i) a.os[i] = shape->o_stride[i];
+  a.B = qa.B;
+  a.Sq = qa.Sq;
+  a.Skv = qa.Skv;
+  a.Hq = qa.Hq;
+  a.Hkv = qa.Hkv;
+  a.s_pad = L.s_pad;
+  a.n_qblk = L.n_qblk;
+  a.n_kblk = L.n_kblk;
+  a.q_block = recipe->q_block;
+  a.k_block = recipe->k_block;
+  a.qk_int8 = qa.qk_int8;
+  a.sm_scale = sm_scale;
+  a.o_fp32 = o_dtype == ATTN_DTYPE_FP32;
+  unsigned long long* counter = reinterpret_cast<unsigned long long*>(skipped_tiles);
+  if (counter && (rc = launched(launch_zero_u64(counter, st), "counter reset"))) return rc;
+  if (threshold_factor > 0.0f) {
+    a.skip = 1;
+    a.log2_lambda = (float)std::log2((double)threshold_factor / (double)shape->S_kv);
+    a.bitmap = skip_bitmap;
+    a.counter = counter;
+  } else if (skip_bitmap) {
+    // lambda = 0: nothing can be skipped; the plain SAGE kernel runs.
+    const int64_t nqb = (shape->S_q + kWaveRows - 1) / kWaveRows;
+    const int64_t nkt = (shape->S_kv + kBlockN - 1) / kBlockN;
+    const size_t n = (size_t)(shape->B * shape->Hq * nqb * nkt);
+    if ((rc = launched(launch_fill_u8(skip_bitmap, n, 0, st), "bitmap clear"))) return rc;
+  }
+  return launched(launch_fmha_sage(a, st), a.skip ? "SAGE skip-softmax attention" : "SAGE attention");
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,41 +412,17 @@ int sage_quantize(const void* q, const void* k, const void* v, const attn_shape*
 
 int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype, const attn_shape* shape,
               const attn_recipe* recipe, float sm_scale, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
-  if (rc) return rc;
-  attn_sage_layout L;
-  if ((rc = check_recipe(recipe))) return rc;
-  if (empty(shape)) return ok();
-  if ((rc = check_sage(q, k, v, shape, recipe, ws, ws_bytes, &L))) return rc;
-  if ((rc = check_ptrs(q, k, v, o))) return rc;
-  if ((rc = check_device_ptr(ws, "workspace"))) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const SageQuantArgs qa = quant_args(q, k, v, shape, recipe, ws, L);
-  if ((rc = launched(launch_sage_quantize(qa, st), "SAGE quantization"))) return rc;
-  FmhaSageArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.q_codes = qa.q_codes;
-  a.k_codes = qa.k_codes;
-  a.v_codes = qa.v_codes;
-  a.q_scale = qa.q_scale;
-  a.k_scale = qa.k_scale;
-  a.v_scale = qa.v_scale;
-  a.o = o;
-  for (int i = 0; i < 3; ++i) a.os[i] = shape->o_stride[i];
-  a.B = qa.B;
-  a.Sq = qa.Sq;
-  a.Skv = qa.Skv;
-  a.Hq = qa.Hq;
-  a.Hkv = qa.Hkv;
-  a.s_pad = L.s_pad;
-  a.n_qblk = L.n_qblk;
-  a.n_kblk = L.n_kblk;
-  a.q_block = recipe->q_block;
-  a.k_block = recipe->k_block;
-  a.qk_int8 = qa.qk_int8;
-  a.sm_scale = sm_scale;
-  a.o_fp32 = o_dtype == ATTN_DTYPE_FP32;
-  return launched(launch_fmha_sage(a, st), "SAGE attention");
+  return run_sage(q, k, v, o, o_dtype, shape, recipe, sm_scale, 0.0f, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int attn_sage_skip_softmax(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
+                           const attn_shape* shape, const attn_recipe* recipe, float sm_scale,
+                           float threshold_factor, uint8_t* skip_bitmap, uint64_t* skipped_tiles, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!(std::isfinite(threshold_factor) && threshold_factor >= 0.0f))
+    return fail(ATTN_ERR_BAD_THRESHOLD, "threshold factor must be finite and >= 0");
+  return run_sage(q, k, v, o, o_dtype, shape, recipe, sm_scale, threshold_factor, skip_bitmap, skipped_tiles, ws,
+                  ws_bytes, stream);
 }
 
 }  // extern "C"

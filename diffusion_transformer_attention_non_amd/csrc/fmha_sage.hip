@@ -22,6 +22,14 @@
 //   O.  Only if m - mo would leave the safe range is O rescaled, exactly.
 //   Epilogue O = acc * sv_d / l (bmm2 scale).
 //
+// Skip-Softmax (kSkip; both options in one kernel, "TRTLLM Attention",
+// section "Skip-Softmax", and "VisualGen Quantized Attention", section
+// "Interaction With Other Features"): after BMM1 of a KV tile the wavefront
+// drops the tile (no exponentials, no BMM2, no change of m) when every valid
+// row i has 2^(M_it - m_i) < lambda, M_it being the row's largest L in the
+// tile and m_i its running maximum over the tiles kept so far; lambda =
+// factor / S_kv.  The first tile is kept.
+//
 // K codes, V^T codes and the tile's 64 K scales stream into a 4-stage LDS
 // ring with buffer_load ... lds, three tiles ahead (out-of-range reads are
 // zero); one barrier per tile.  LDS layouts (16-byte chunks, XOR-swizzled so
@@ -66,7 +74,7 @@ __device__ __forceinline__ int sage_key_of_row(int row) {
 }
 
 // kBlock4: k_block >= 4, so each group of 4 keys (aligned) shares one K scale.
-template <bool kInt8, bool kBlock4>
+template <bool kInt8, bool kBlock4, bool kSkip>
 __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageB];
@@ -177,6 +185,16 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   float m = kNegInf, mo = kNegInf;   // reference and O reference (integers, log2 units)
   int bsc = 127;                      // E8M0 scale 2^(m - mo)
 
+  // Skip-Softmax state: exact running maximum of L over kept tiles, the
+  // wavefront's skipped-tile count and its bitmap row.
+  float mrun = kNegInf;
+  unsigned skipped = 0;
+  const bool qvalid = q0 + l32 < Sq;
+  uint8_t* bitmap_row = nullptr;
+  if (kSkip && p.bitmap != nullptr && q0 < Sq)
+    bitmap_row = p.bitmap + ((int64_t)(b * p.Hq + h) * ((Sq + kSageWaveRows - 1) / kSageWaveRows) +
+                             q0 / kSageWaveRows) * nkt;
+
   // BMM1 of the tile in stage sm into s: S^T of keys 32 hh + 16 kb + r
   // (register r of block kb); int8 accumulators are converted to float.
   auto bmm1 = [&](const uint8_t* sm, f32x16 (&s)[2]) __attribute__((always_inline)) {
@@ -242,8 +260,20 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+    const float lmax = max_halves(mx) * qsc;   // row maximum of L over the tile
+    if constexpr (kSkip) {
+      const int t = key0 / kBlockN;
+      const bool keep = t == 0 || __any(qvalid && !(lmax - mrun < p.log2_lambda));
+      if (bitmap_row != nullptr && lane == 0) bitmap_row[t] = keep ? 0 : 1;
+      if (!keep) {   // wavefront-uniform: a real branch around the rest of the tile
+        asm volatile("");
+        ++skipped;
+        return;
+      }
+      mrun = fmaxf(mrun, lmax);
+    }
     // Reference update.
-    const float mnew = fmaxf(m, __builtin_ceilf(max_halves(mx) * qsc));
+    const float mnew = fmaxf(m, __builtin_ceilf(lmax));
     if (__any(mnew > m)) {
       if (m == kNegInf) mo = mnew;   // the first tile fixes the O reference
       m = mnew;
@@ -317,6 +347,8 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     if (t + 4 >= nkt) break;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (kSkip && p.counter != nullptr && lane == 0 && q0 < Sq && skipped)
+    atomicAdd(p.counter, (unsigned long long)skipped);
 
   // ---- Epilogue: O = O^T * sv_d / l.
   const float* svp = p.v_scale + ((int64_t)b * p.Hkv + g) * kHeadDim;
@@ -351,12 +383,20 @@ hipError_t launch_fmha_sage(const FmhaSageArgs& a, hipStream_t stream) {
   if (nwg <= 0) return hipSuccess;
   const dim3 grid((unsigned)nwg), block(kSageWaves * 64);
   const bool b4 = a.k_block % 4 == 0;
-  if (a.qk_int8) {
-    if (b4) hipLaunchKernelGGL((fmha_sage_kernel<true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fmha_sage_kernel<true, false>), grid, block, 0, stream, a);
+  if (a.skip) {
+    if (a.qk_int8) {
+      if (b4) hipLaunchKernelGGL((fmha_sage_kernel<true, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fmha_sage_kernel<true, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (b4) hipLaunchKernelGGL((fmha_sage_kernel<false, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((fmha_sage_kernel<false, false, true>), grid, block, 0, stream, a);
+    }
+  } else if (a.qk_int8) {
+    if (b4) hipLaunchKernelGGL((fmha_sage_kernel<true, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fmha_sage_kernel<true, false, false>), grid, block, 0, stream, a);
   } else {
-    if (b4) hipLaunchKernelGGL((fmha_sage_kernel<false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fmha_sage_kernel<false, false>), grid, block, 0, stream, a);
+    if (b4) hipLaunchKernelGGL((fmha_sage_kernel<false, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((fmha_sage_kernel<false, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

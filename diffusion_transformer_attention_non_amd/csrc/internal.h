@@ -72,6 +72,10 @@ struct FmhaSageArgs {
   int qk_int8;
   float sm_scale;
   int o_fp32;
+  int skip;                         // 1 = Skip-Softmax tile test on (32 rows x one KV tile)
+  float log2_lambda;                // skip threshold in log2 units
+  uint8_t* bitmap;                  // nullable, [B, Hq, ceil(Sq / 32), ceil(Skv / 64)]
+  unsigned long long* counter;      // nullable
 };
 
 hipError_t launch_fmha_sage(const FmhaSageArgs& a, hipStream_t stream);

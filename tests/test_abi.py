@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert "attn_dense_bf16" in names and "sage_quantize" in names and len(names) == 9
+    assert "attn_dense_bf16" in names and "attn_sage_skip_softmax" in names and len(names) == 10
     out = subprocess.run(["nm", "-D", "--defined-only", dit.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     missing = [n for n in names if n not in exported]
@@ -169,3 +169,18 @@ def test_sage_workspace_checked_before_device():
                              None) == LAYOUT
     assert lib.attn_sage(FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(_recipe(2, 3, 16)), 0.1, ws, 1 << 30,
                          None) == RECIPE
+
+
+def test_sage_skip_threshold_and_workspace_checked_before_device():
+    lib = dit._lib()
+    s = _shape()
+    rec = _recipe(2, 1, 16)
+    ws = ctypes.c_void_p(0x200000)
+    F = ctypes.c_float
+    call = lambda factor, wsb=1 << 30, r=rec: lib.attn_sage_skip_softmax(
+        FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(r), F(0.1), F(factor), None, None, ws, wsb, None)
+    assert call(-1.0) == THRESHOLD
+    assert call(float("nan")) == THRESHOLD
+    assert call(float("inf")) == THRESHOLD
+    assert call(1.0, wsb=10) == WS
+    assert call(1.0, r=_recipe(2, 3, 16)) == RECIPE

@@ -1,0 +1,122 @@
+"""SAGE attention with the Skip-Softmax tile test on the GPU against the
+oracle's combined emulation (skip sets compared outside a threshold band)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_non_amd as dit
+from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate, positional_qkv
+from oracle import sage_quantize, sage_skip_attention
+from tests._gpu_util import announce, needs_gpu, rel_l2, to_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+SC = 1 / math.sqrt(128)
+NORTH_STAR_BAND = 1e-6      # |2^(M - m) - lambda| within this of the threshold is exempt
+LOG2_BAND = 1e-4            # binary32 rounding of L (a scaled int32 or fp32-accumulated dot) in log2 units
+
+
+def _compare(got, ref_skip, ratio, lam):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        near = (np.abs(ratio - lam) <= NORTH_STAR_BAND) | (np.abs(np.log2(ratio) - math.log2(lam)) <= LOG2_BAND)
+    near &= ~np.isnan(ratio)
+    diff = (got != ref_skip) & ~near
+    assert not diff.any(), f"{int(diff.sum())} tiles differ outside the band (band tiles: {int(near.sum())})"
+    return int(((got != ref_skip) & near).sum())
+
+
+def _gqa(q, k, v, Hkv):
+    """Keep Hkv of the K/V heads (query head h reads KV head h // (Hq / Hkv))."""
+    sel = list(range(0, k.shape[2], k.shape[2] // Hkv))[:Hkv]
+    return q, k[:, :, sel].contiguous(), v[:, :, sel].contiguous()
+
+
+@pytest.mark.parametrize("dt,qb,kb", [("int8", 1, 16), ("fp8", 1, 4)])
+def test_factor_zero_is_bit_identical_to_sage(dt, qb, kb):
+    announce(f"sage-skip factor 0 vs sage {dt}")
+    q, k, v = positional_qkv(grid=(2, 8, 24), H=2, seed=1)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    rec = dit.SageRecipe(dt, "fp8", qb, kb, 1)
+    ref = dit.attn_sage(qd, kd, vd, rec)
+    o, ex = dit.attn_sage_skip_softmax(qd, kd, vd, rec, 0.0, return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+    assert int(ex["bitmap"].sum()) == 0 and int(ex["skipped"][0]) == 0
+
+
+CASES = [((2, 8, 24), 2, 2, "int8", 1, 16, 1.0), ((2, 8, 24), 2, 2, "fp8", 1, 4, 10.0),
+         ((2, 8, 24), 2, 2, "fp8", 1, 1, 100.0), ((3, 9, 17), 4, 2, "int8", 4, 1, 30.0),
+         ((1, 1, 200), 2, 1, "fp8", 16, 16, 50.0)]
+
+
+@pytest.mark.parametrize("grid,Hq,Hkv,dt,qb,kb,factor", CASES)
+def test_skip_set_and_output_match_oracle(grid, Hq, Hkv, dt, qb, kb, factor):
+    announce(f"sage-skip grid={grid} Hq={Hq} Hkv={Hkv} {dt} ({qb},{kb}) factor={factor}")
+    q, k, v = _gqa(*positional_qkv(grid=grid, H=Hq, seed=2), Hkv)
+    S = q.shape[1]
+    rec = dit.SageRecipe(dt, "fp8", qb, kb, 1)
+    o, ex = dit.attn_sage_skip_softmax(q.cuda(), k.cuda(), v.cuda(), rec, factor, out_dtype=torch.float32,
+                                       return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    bm, _ = dit.tile_config()
+    quant = sage_quantize(q, k, v, dt, qb, kb)
+    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, factor, bm, dit.kv_tile())
+    got = ex["bitmap"].cpu().numpy().astype(bool)
+    assert got.shape == skipped.shape
+    flips = _compare(got, skipped, ratio, factor / S)
+    assert int(ex["skipped"][0]) == int(got.sum())
+    assert not got[..., 0].any()
+    assert skipped.any()
+    r = rel_l2(to_np(o)[:, rows], ref)
+    assert r <= 3e-2, r
+    if flips == 0:
+        assert r <= 5e-3, r
+
+
+def test_gaussian_inputs_rarely_skip():
+    announce("sage-skip gaussian inputs")
+    q, k, v = gaussian_qkv(1, 1000, 2, 1, seed=9, k_bias_std=4.0, outliers=4)
+    rec = dit.SageRecipe("fp8", "fp8", 1, 4, 1)
+    o, ex = dit.attn_sage_skip_softmax(q.cuda(), k.cuda(), v.cuda(), rec, 1.0, out_dtype=torch.float32,
+                                       return_bitmap=True)
+    torch.cuda.synchronize()
+    quant = sage_quantize(q, k, v, "fp8", 1, 4)
+    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 1.0, dit.tile_config()[0], dit.kv_tile())
+    flips = _compare(ex["bitmap"].cpu().numpy().astype(bool), skipped, ratio, 1.0 / 1000)
+    r = rel_l2(to_np(o), ref)
+    assert r <= 3e-2 and (flips or r <= 5e-3), r
+
+
+def test_invalid_threshold_rejected():
+    q, k, v = gaussian_qkv(1, 8, 1, 1, seed=0)
+    rec = dit.SageRecipe("int8", "fp8", 1, 16, 1)
+    for bad in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(ValueError, match="THRESHOLD"):
+            dit.attn_sage_skip_softmax(q.cuda(), k.cuda(), v.cuda(), rec, bad)
+
+
+def test_wan_shape_sampled_tiles():
+    """B=1, H=40, S=75,600 (21 x 45 x 80 grid), spatially peaked Q/K, FP8 (1, 4, 1); sampled query tiles."""
+    announce("sage-skip wan S=75600 H=40 generate")
+    qd, kd, vd = generate("skip_wan_b1_h40_s75600", device="cuda")
+    q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
+    rec = dit.SageRecipe("fp8", "fp8", 1, 4, 1)
+    bm, _ = dit.tile_config()
+    S = q.shape[1]
+    nqb = -(-S // bm)
+    heads = [0, 39]
+    qtiles = np.array([0, 1234, nqb - 1])
+    quants = {h: sage_quantize(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], "fp8", 1, 4) for h in heads}
+    for factor in (1.0, 100.0):
+        announce(f"sage-skip wan factor={factor}")
+        o, ex = dit.attn_sage_skip_softmax(qd, kd, vd, rec, factor, return_bitmap=True, return_count=True)
+        torch.cuda.synchronize()
+        bitmap = ex["bitmap"].cpu().numpy().astype(bool)
+        assert int(ex["skipped"][0]) == int(bitmap.sum())
+        for h in heads:
+            ref, skipped, ratio, rows = sage_skip_attention(quants[h], SC, factor, bm, dit.kv_tile(), qtiles=qtiles)
+            _compare(bitmap[:, h:h + 1, qtiles], skipped, ratio, factor / S)
+            r = rel_l2(to_np(o[:, rows, h:h + 1]), ref)
+            assert r <= 3e-2, (factor, h, r)
+        print(f"factor {factor}: skipped fraction {bitmap.mean():.4f}")
