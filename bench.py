@@ -254,6 +254,21 @@ def main():
             sweep[str(f)] = {"ms": ms, "effective_tflops": F / ms / 1e9, "skip_fraction": frac,
                              "algorithmic_tflops": (2 + 2 * (1 - frac)) * B * H * S * S * D / ms / 1e9}
         extra["skip_factor_sweep_wan"] = sweep
+        # SAGE FP8 (1,4,1) with Skip-Softmax on the same spatially peaked inputs
+        # (quantization included); votes are 32 rows x one 64-key KV tile.
+        sweep = {}
+        sage_votes = B * H * -(-S // vote_m) * -(-S // dit.kv_tile())
+        for f in (0.0, 1.0, 10.0, 100.0):
+            cnt = {}
+
+            def run_sf(f=f, cnt=cnt):
+                _, ex = dit.attn_sage_skip_softmax(q5, k5, v5, rec, f, out=o_sage, workspace=ws, return_count=True)
+                cnt["n"] = ex["skipped"]
+            ms = timed_calls(run_sf, 2, torch)
+            frac = float(cnt["n"][0]) / sage_votes
+            sweep[str(f)] = {"ms": ms, "effective_tflops": F / ms / 1e9, "skip_fraction": frac,
+                             "algorithmic_tflops": (2 + 2 * (1 - frac)) * B * H * S * S * D / ms / 1e9}
+        extra["sage_fp8_skip_factor_sweep_wan"] = sweep
         del q4, k4, v4, ws, o_sage
         q2, k2, v2 = generate("dense_gqa_b2_h24kv8_s8192", device=dev)
         ms = timed_calls(lambda: dit.attn_dense_bf16(q2, k2, v2), 5, torch)

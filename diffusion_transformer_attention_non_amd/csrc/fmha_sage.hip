@@ -179,8 +179,9 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   f32x16 lrow;
 #pragma unroll
   for (int r = 0; r < 16; ++r) lrow[r] = 0.0f;
-  const i32x8 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+  i32x8 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                 0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+  asm volatile("" : "+v"(ones8));   // kept in registers, not rebuilt before every use
 
   float m = kNegInf, mo = kNegInf;   // reference and O reference (integers, log2 units)
   int bsc = 127;                      // E8M0 scale 2^(m - mo)
@@ -298,7 +299,9 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = exp2_fast(__builtin_fmaf(s[kb][r0 + j], qsc, nb));
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __builtin_bit_cast(int, x[3]), false);
+      // The low half is written over x[0]'s own register (x[0] is dead after
+      // this), so no copy of an "old" value is needed.
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __builtin_bit_cast(int, x[0]), false);
       pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
     }
     // BMM2 and row sums, P scaled by 2^(m - mo).
