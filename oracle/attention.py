@@ -12,7 +12,8 @@ taken here).  Attention is non-causal and unmasked (TRTLLM Attention,
 Parity status:
   exact_attention   pinned: brute force on tiny shapes, torch SDPA in float64,
                     closed forms (constant V, Q = 0, one dominant key),
-                    permutation invariance, rows of P summing to 1.
+                    permutation invariance, rows of P summing to 1; its LSE
+                    against scipy's logsumexp and ln(S_kv) at Q = 0.
   k_channel_mean    pinned: closed-form error bound against the float64 mean,
                     exact on constant channels.
   sage_quantize     pinned: softmax invariance of the smoothing, round-trip
@@ -26,7 +27,7 @@ Parity status:
                     skip_attention on the dequantized inputs; monotone in the
                     factor; first tile never skipped; a dominant first tile
                     skips every later one.
-  skip_attention    pinned: factor 0 equals exact attention, monotone skip
+  skip_attention    pinned: factor 0 equals exact attention (LSE too), monotone skip
                     sets, first tile never skipped, scalar brute force on tiny
                     grids, dropped-mass error bound, a constructed case where
                     every later tile is skipped.
@@ -83,7 +84,7 @@ def _round_out(o, out_dtype):
 # Exact attention
 # ----------------------------------------------------------------------------
 
-def exact_attention(q, k, v, sm_scale, rows=None, out_dtype=None, return_probs=False):
+def exact_attention(q, k, v, sm_scale, rows=None, out_dtype=None, return_probs=False, return_lse=False):
     """O = softmax(sm_scale * Q K^T) V per (batch, query head), in float64.
 
     The plain definition of the fused multi-head attention that the pages'
@@ -93,7 +94,9 @@ def exact_attention(q, k, v, sm_scale, rows=None, out_dtype=None, return_probs=F
 
     ``rows`` selects query rows (the same for every batch entry and head).
     Returns O as [B, R, Hq, D] float64, and with ``return_probs`` also the
-    normalized probabilities [B, Hq, R, S_kv].
+    normalized probabilities [B, Hq, R, S_kv]; with ``return_lse`` also the
+    row log-sum-exp LSE_i = ln sum_j exp(s_ij) [B, Hq, R] (natural log, the
+    quantity that merges partial attention results over key subsets).
     """
     qf, kf, vf = _f64(q), _f64(k), _f64(v)
     B, Sq, Skv, Hq, Hkv, D = _shape_check(qf, kf, vf)
@@ -102,6 +105,7 @@ def exact_attention(q, k, v, sm_scale, rows=None, out_dtype=None, return_probs=F
     R = len(rows)
     out = np.empty((B, R, Hq, D))
     probs = np.empty((B, Hq, R, Skv)) if return_probs else None
+    lse = np.empty((B, Hq, R))
     step = max(1, _ROW_CHUNK_ELEMS // max(1, Skv))
     for b in range(B):
         for h in range(Hq):
@@ -109,13 +113,16 @@ def exact_attention(q, k, v, sm_scale, rows=None, out_dtype=None, return_probs=F
             for r0 in range(0, R, step):
                 rr = rows[r0:r0 + step]
                 s = sm_scale * (qf[b, rr, h, :] @ kg.T)
-                p = np.exp(s - s.max(axis=1, keepdims=True))
+                mx = s.max(axis=1, keepdims=True)
+                p = np.exp(s - mx)
                 l = p.sum(axis=1, keepdims=True)
                 out[b, r0:r0 + step, h, :] = (p @ vg) / l
+                lse[b, h, r0:r0 + step] = (mx + np.log(l))[:, 0]
                 if return_probs:
                     probs[b, h, r0:r0 + step, :] = p / l
     out = _round_out(out, out_dtype)
-    return (out, probs) if return_probs else out
+    res = (out,) + ((probs,) if return_probs else ()) + ((lse,) if return_lse else ())
+    return res if len(res) > 1 else out
 
 
 # ----------------------------------------------------------------------------
@@ -372,7 +379,7 @@ def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, 
 # Skip-Softmax
 # ----------------------------------------------------------------------------
 
-def skip_attention(q, k, v, sm_scale, factor, block_m, block_n, qtiles=None, out_dtype=None):
+def skip_attention(q, k, v, sm_scale, factor, block_m, block_n, qtiles=None, out_dtype=None, return_lse=False):
     """Skip-Softmax attention in float64, with its skipped-tile set.
 
     The pages define the threshold as factor / seqlen (the knob to
@@ -389,7 +396,8 @@ def skip_attention(q, k, v, sm_scale, factor, block_m, block_n, qtiles=None, out
       attention over the kept keys only.
     ``qtiles`` selects query tiles (default: all).  Returns (O [B, R, Hq, D]
     for the rows of the selected tiles, skipped [B, Hq, nQT, T] bool,
-    ratio [B, Hq, nQT, T] = max_i exp(M_it - m_i) with NaN at t = 0, rows).
+    ratio [B, Hq, nQT, T] = max_i exp(M_it - m_i) with NaN at t = 0, rows),
+    plus the LSE [B, Hq, R] over the kept keys with ``return_lse``.
     """
     qf, kf, vf = _f64(q), _f64(k), _f64(v)
     B, Sq, Skv, Hq, Hkv, D = _shape_check(qf, kf, vf)
@@ -401,6 +409,7 @@ def skip_attention(q, k, v, sm_scale, factor, block_m, block_n, qtiles=None, out
     ln_lam = math.log(lam) if lam > 0 else -math.inf
     rows = np.concatenate([np.arange(t * block_m, min(Sq, (t + 1) * block_m)) for t in qtiles])
     out = np.empty((B, len(rows), Hq, D))
+    lse = np.empty((B, Hq, len(rows)))
     skipped = np.zeros((B, Hq, len(qtiles), T), bool)
     ratio = np.full((B, Hq, len(qtiles), T), np.nan)
     tile_starts = np.arange(0, Skv, block_n)
@@ -424,10 +433,14 @@ def skip_attention(q, k, v, sm_scale, factor, block_m, block_n, qtiles=None, out
                     m = np.maximum(m, M[:, t])
                 keep = ~skipped[b, h, qi][tile_of_key]                     # [S_kv]
                 sk = np.where(keep[None, :], s, -np.inf)
-                p = np.exp(sk - sk.max(axis=1, keepdims=True))
-                out[b, r0:r0 + len(rr), h, :] = (p @ vg) / p.sum(axis=1, keepdims=True)
+                mx = sk.max(axis=1, keepdims=True)
+                p = np.exp(sk - mx)
+                l = p.sum(axis=1, keepdims=True)
+                out[b, r0:r0 + len(rr), h, :] = (p @ vg) / l
+                lse[b, h, r0:r0 + len(rr)] = (mx + np.log(l))[:, 0]
                 r0 += len(rr)
-    return _round_out(out, out_dtype), skipped, ratio, rows
+    res = (_round_out(out, out_dtype), skipped, ratio, rows)
+    return res + (lse,) if return_lse else res
 
 
 def skip_gate_enabled(t, D):

@@ -104,3 +104,42 @@ def test_gqa_group_shares_kv_head():
         g = h // 3
         oh = exact_attention(q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1], 0.1)
         np.testing.assert_allclose(o[:, :, h:h + 1], oh, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- LSE
+
+@pytest.mark.parametrize("Sq,Skv,Hq,Hkv", [(5, 9, 2, 1), (33, 17, 4, 2)])
+def test_lse_matches_scipy_logsumexp(Sq, Skv, Hq, Hkv):
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((1, Sq, Hq, 128)) * 2
+    k = rng.standard_normal((1, Skv, Hkv, 128)) * 2
+    v = rng.standard_normal((1, Skv, Hkv, 128))
+    _, lse = exact_attention(q, k, v, 0.3, return_lse=True)
+    G = Hq // Hkv
+    for h in range(Hq):
+        logits = 0.3 * np.einsum("id,jd->ij", q[0, :, h], k[0, :, h // G])
+        np.testing.assert_allclose(lse[0, h], logsumexp(logits, axis=1), rtol=0, atol=1e-12)
+
+
+def test_lse_zero_q_is_log_of_key_count():
+    rng = np.random.default_rng(22)
+    k = rng.standard_normal((2, 37, 1, 128))
+    v = rng.standard_normal((2, 37, 1, 128))
+    _, lse = exact_attention(np.zeros((2, 5, 3, 128)), k, v, 0.1, return_lse=True)
+    np.testing.assert_allclose(lse, np.full((2, 3, 5), math.log(37)), rtol=0, atol=1e-13)
+
+
+def test_lse_merges_partial_results_over_key_subsets():
+    """The property LSE is exported for: attention over keys A u B equals the
+    LSE-weighted merge of the results over A and over B."""
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((1, 7, 1, 128))
+    k = rng.standard_normal((1, 40, 1, 128))
+    v = rng.standard_normal((1, 40, 1, 128))
+    o, lse = exact_attention(q, k, v, 0.2, return_lse=True)
+    oa, la = exact_attention(q, k[:, :13], v[:, :13], 0.2, return_lse=True)
+    ob, lb = exact_attention(q, k[:, 13:], v[:, 13:], 0.2, return_lse=True)
+    wa, wb = np.exp(la - lse)[0, 0], np.exp(lb - lse)[0, 0]
+    np.testing.assert_allclose(wa + wb, 1.0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o[0, :, 0], wa[:, None] * oa[0, :, 0] + wb[:, None] * ob[0, :, 0], rtol=0, atol=1e-13)

@@ -128,3 +128,18 @@ def test_gate_truth_table(t, D, on):
 def test_gate_rejects_bad_values(t, D):
     with pytest.raises(ValueError):
         skip_gate_enabled(t, D)
+
+
+def test_lse_factor_zero_and_kept_key_set(peaked):
+    q, k, v = peaked
+    _, _, _, rows, lse0 = skip_attention(q, k, v, SC, 0.0, 32, 32, return_lse=True)
+    _, lse_exact = exact_attention(q, k, v, SC, rows=rows, return_lse=True)
+    np.testing.assert_allclose(lse0, lse_exact, rtol=0, atol=1e-12)
+    # with skipping, the LSE is that of exact attention over the kept keys of each query tile
+    _, sk, _, rows, lse = skip_attention(q, k, v, SC, 100.0, 32, 32, qtiles=[3], return_lse=True)
+    keep = ~sk[0, :, 0]                              # [Hq, T]
+    for h in range(q.shape[2]):
+        keys = np.flatnonzero(np.repeat(keep[h], 32)[:k.shape[1]])
+        _, ref = exact_attention(q[:, :, h:h + 1], k[:, keys, h:h + 1], v[:, keys, h:h + 1], SC, rows=rows,
+                                 return_lse=True)
+        np.testing.assert_allclose(lse[0, h], ref[0, 0], rtol=0, atol=1e-12)
