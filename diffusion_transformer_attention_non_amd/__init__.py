@@ -88,11 +88,11 @@ def _lib():
         P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         SP, RP, LP = ctypes.POINTER(_Shape), ctypes.POINTER(_Recipe), ctypes.POINTER(_Layout)
         sig = {
-            "attn_dense_bf16": [P, P, P, P, I, SP, F, P],
+            "attn_dense_bf16": [P, P, P, P, I, SP, F, P, P],
             "attn_sage_layout_query": [SP, RP, LP],
             "sage_quantize": [P, P, P, SP, RP, P, ctypes.c_size_t, P],
             "attn_sage": [P, P, P, P, I, SP, RP, F, P, ctypes.c_size_t, P],
-            "attn_skip_softmax": [P, P, P, P, I, SP, F, F, P, P, P],
+            "attn_skip_softmax": [P, P, P, P, I, SP, F, F, P, P, P, P],
             "attn_sage_skip_softmax": [P, P, P, P, I, SP, RP, F, F, P, P, P, ctypes.c_size_t, P],
             "attn_skip_gate": [F, F, ctypes.POINTER(I)],
             "attn_tile_config": [ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
@@ -179,14 +179,27 @@ def _scale(q, sm_scale):
     return 1.0 / math.sqrt(q.shape[-1]) if sm_scale is None else float(sm_scale)
 
 
-def attn_dense_bf16(q, k, v, out=None, out_dtype=torch.bfloat16, sm_scale=None):
-    """Dense non-causal attention softmax(sm_scale Q K^T) V, BF16 inputs."""
+def _lse_buffer(q, want):
+    if not want:
+        return None
+    B, Sq, Hq, _ = q.shape
+    return torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+
+
+def attn_dense_bf16(q, k, v, out=None, out_dtype=torch.bfloat16, sm_scale=None, return_lse=False):
+    """Dense non-causal attention softmax(sm_scale Q K^T) V, BF16 inputs.
+
+    With ``return_lse`` returns (out, lse), lse [B, Hq, S_q] float32 holding
+    ln sum_j exp(sm_scale <q_i, k_j>) per row.
+    """
     _check_tensors(q, k, v)
     out, odt = _out(q, out, out_dtype)
     shape = _shape(q, k, v, out)
+    lse = _lse_buffer(q, return_lse)
     _check(_lib().attn_dense_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), odt,
-                                  ctypes.byref(shape), _scale(q, sm_scale), _stream(q)))
-    return out
+                                  ctypes.byref(shape), _scale(q, sm_scale),
+                                  lse.data_ptr() if lse is not None else None, _stream(q)))
+    return (out, lse) if return_lse else out
 
 
 @dataclass(frozen=True)
@@ -292,12 +305,13 @@ def attn_sage(q, k, v, recipe: SageRecipe = SageRecipe(), out=None, out_dtype=to
 
 
 def attn_skip_softmax(q, k, v, threshold_factor, out=None, out_dtype=torch.bfloat16, sm_scale=None,
-                      return_bitmap=False, return_count=False):
+                      return_bitmap=False, return_count=False, return_lse=False):
     """Skip-Softmax attention with threshold = threshold_factor / S_kv.
 
     Returns out, or (out, extras) with extras holding "bitmap" (uint8
-    [B, Hq, ceil(S_q/block_m), ceil(S_kv/block_n)], 1 = skipped) and/or
-    "skipped" (a one-element int64 tensor) when requested.
+    [B, Hq, ceil(S_q/block_m), ceil(S_kv/block_n)], 1 = skipped), "skipped"
+    (a one-element int64 tensor) and/or "lse" ([B, Hq, S_q] float32, over the
+    kept keys) when requested.
     """
     _check_tensors(q, k, v)
     out, odt = _out(q, out, out_dtype)
@@ -309,17 +323,21 @@ def attn_skip_softmax(q, k, v, threshold_factor, out=None, out_dtype=torch.bfloa
         bitmap = torch.empty((B, Hq, -(-Sq // bm), -(-k.shape[1] // bn)), dtype=torch.uint8, device=q.device)
     if return_count:
         cnt = torch.empty(1, dtype=torch.int64, device=q.device)
+    lse = _lse_buffer(q, return_lse)
     _check(_lib().attn_skip_softmax(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), odt,
                                     ctypes.byref(shape), _scale(q, sm_scale), float(threshold_factor),
                                     bitmap.data_ptr() if bitmap is not None else None,
-                                    cnt.data_ptr() if cnt is not None else None, _stream(q)))
-    if not (return_bitmap or return_count):
+                                    cnt.data_ptr() if cnt is not None else None,
+                                    lse.data_ptr() if lse is not None else None, _stream(q)))
+    if not (return_bitmap or return_count or return_lse):
         return out
     extras = {}
     if bitmap is not None:
         extras["bitmap"] = bitmap
     if cnt is not None:
         extras["skipped"] = cnt
+    if lse is not None:
+        extras["lse"] = lse
     return out, extras
 
 

@@ -130,6 +130,14 @@ int check_ptrs(const void* q, const void* k, const void* v, const void* o) {
   return ATTN_OK;
 }
 
+// The optional LSE output: 4-byte aligned (checked on the host first), device memory.
+int check_lse_align(const float* lse) {
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(ATTN_ERR_BAD_LAYOUT, "lse must be 4-byte aligned");
+  return ATTN_OK;
+}
+int check_lse(const float* lse) { return lse ? check_device_ptr(lse, "lse") : ATTN_OK; }
+
 FmhaBf16Args bf16_args(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
                        const attn_shape* s, float sm_scale) {
   FmhaBf16Args a;
@@ -343,25 +351,29 @@ int attn_skip_gate(float t, float disabled_until_timestep, int* enabled) {
 }
 
 int attn_dense_bf16(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
-                    const attn_shape* shape, float sm_scale, void* stream) {
+                    const attn_shape* shape, float sm_scale, float* lse, void* stream) {
   int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
   if (rc) return rc;
   if (empty(shape)) return ok();
   if ((rc = check_kv_span(shape))) return rc;
+  if ((rc = check_lse_align(lse))) return rc;
   if ((rc = check_ptrs(q, k, v, o))) return rc;
-  const FmhaBf16Args a = bf16_args(q, k, v, o, o_dtype, shape, sm_scale);
+  if ((rc = check_lse(lse))) return rc;
+  FmhaBf16Args a = bf16_args(q, k, v, o, o_dtype, shape, sm_scale);
+  a.lse = lse;
   return launched(launch_fmha_bf16(a, static_cast<hipStream_t>(stream)), "dense attention");
 }
 
 int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
                       const attn_shape* shape, float sm_scale, float threshold_factor, uint8_t* skip_bitmap,
-                      uint64_t* skipped_tiles, void* stream) {
+                      uint64_t* skipped_tiles, float* lse, void* stream) {
   int rc = check_common(q, k, v, o, o_dtype, shape, sm_scale);
   if (rc) return rc;
   if (!(std::isfinite(threshold_factor) && threshold_factor >= 0.0f))
     return fail(ATTN_ERR_BAD_THRESHOLD, "threshold factor must be finite and >= 0");
   if (empty(shape)) return ok();
   if ((rc = check_kv_span(shape))) return rc;
+  if ((rc = check_lse_align(lse))) return rc;
   if ((rc = check_ptrs(q, k, v, o))) return rc;
   if (skip_bitmap && (rc = check_device_ptr(skip_bitmap, "skip_bitmap"))) return rc;
   if (skipped_tiles) {
@@ -369,8 +381,10 @@ int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn
       return fail(ATTN_ERR_BAD_LAYOUT, "skipped_tiles must be 8-byte aligned");
     if ((rc = check_device_ptr(skipped_tiles, "skipped_tiles"))) return rc;
   }
+  if ((rc = check_lse(lse))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   FmhaBf16Args a = bf16_args(q, k, v, o, o_dtype, shape, sm_scale);
+  a.lse = lse;
   unsigned long long* counter = reinterpret_cast<unsigned long long*>(skipped_tiles);
   if (counter && (rc = launched(launch_zero_u64(counter, st), "counter reset"))) return rc;
   if (threshold_factor == 0.0f) {

@@ -44,6 +44,7 @@ namespace {
 constexpr int kDenseWaveRows = 64;   // query rows per wavefront
 constexpr int kDenseWaves = kBlockM / kDenseWaveRows;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the reference max moves
 constexpr int kRowBytes = kHeadDim * 2;                 // one bf16 row of 128 channels
@@ -459,8 +460,12 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float s_lo = __shfl(rsum[qb][0], l32 & 15, 64), s_hi = __shfl(rsum[qb][1], l32 & 15, 64);
-    const float inv = 1.0f / (l32 < 16 ? s_lo : s_hi);
+    const float l = l32 < 16 ? s_lo : s_hi;
+    const float inv = 1.0f / l;
     const int row = q0 + qb * 32 + l32;
+    // LSE = ln(sum_j exp(s_ij)) = (m_ref + log2 l) ln 2, P being 2^(L - m_ref).
+    if (p.lse != nullptr && hh == 0 && row < Sq)
+      p.lse[((int64_t)b * p.Hq + h) * Sq + row] = (mref[qb] + __log2f(l)) * kLn2;
     if (row < Sq) {
       const int64_t obase = b * p.os[0] + (int64_t)row * p.os[1] + h * p.os[2];
 #pragma unroll

@@ -50,6 +50,7 @@ namespace ditattn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before the reference max moves
 constexpr int kRowBytes = kHeadDim * 2;                 // one bf16 row of 128 channels
@@ -322,8 +323,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 1) void fmha_skip_kernel(FmhaBf16
     atomicAdd(p.counter, (unsigned long long)skipped);
 
   // ---- Epilogue: O = O^T / l, lane writes 4 consecutive d per register group.
-  const float inv = 1.0f / sum_halves(lsum);
+  const float lrow = sum_halves(lsum);
+  const float inv = 1.0f / lrow;
   const int row = q0 + l32;
+  // LSE over the kept keys = (m_ref + log2 l) ln 2, P being 2^(L - m_ref).
+  if (p.lse != nullptr && hh == 0 && row < Sq)
+    p.lse[((int64_t)b * p.Hq + h) * Sq + row] = (mref + __log2f(lrow)) * kLn2;
   if (row < Sq) {
     const int64_t obase = b * p.os[0] + (int64_t)row * p.os[1] + h * p.os[2];
 #pragma unroll

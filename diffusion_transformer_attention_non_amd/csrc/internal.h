@@ -28,6 +28,7 @@ struct FmhaBf16Args {
   float log2_lambda;                // skip threshold in log2 units (skip kernel only)
   uint8_t* bitmap;                  // nullable
   unsigned long long* counter;      // nullable
+  float* lse;                       // nullable, [B, Hq, Sq] natural-log row log-sum-exp
 };
 
 hipError_t launch_fmha_bf16(const FmhaBf16Args& a, hipStream_t stream);        // dense

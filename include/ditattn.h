@@ -111,10 +111,18 @@ typedef struct {
  *   1/sqrt(128); INVALID_ARG otherwise).  Errors: INVALID_ARG,
  *   UNSUPPORTED_HEAD_DIM, BAD_GQA,
  *   BAD_LAYOUT, DEVICE.  Empty problems (B, S_q, Hq = 0) return OK with no
- *   launch; S_kv = 0 with S_q > 0 is INVALID_ARG (softmax over no keys). */
+ *   launch; S_kv = 0 with S_q > 0 is INVALID_ARG (softmax over no keys).
+ *   S_q and S_kv are independent (cross-attention: Q from one sequence, K/V
+ *   from another).
+ *   lse (nullable, device, 4-byte aligned): [B, Hq, S_q] fp32, contiguous,
+ *   receives LSE_i = ln sum_j exp(sm_scale <q_i, k_j>) per row: the weight
+ *   that merges attention results over disjoint key sets, as context
+ *   parallelism needs ([VQA] "Interaction With Other Features": the dense
+ *   backend that exports LSE composes with ring / Attention2D parallelism).
+ *   BAD_LAYOUT if misaligned. */
 int attn_dense_bf16(const void* q, const void* k, const void* v, void* o,
                     attn_dtype o_dtype, const attn_shape* shape, float sm_scale,
-                    void* stream);
+                    float* lse, void* stream);
 
 /* Workspace layout for sage_quantize / attn_sage ([VQA] "SageAttention in
  * the TRTLLM backend").  Host-only; fills *out.  Errors as sage_quantize. */
@@ -189,12 +197,13 @@ int attn_sage_skip_softmax(const void* q, const void* k, const void* v, void* o,
  *   skip_bitmap (nullable, device): [B, Hq, ceil(S_q/block_m),
  *   ceil(S_kv/block_n)] uint8, 1 = skipped.  skipped_tiles (nullable,
  *   device): receives the number of skipped (query block, KV tile) pairs.
+ *   lse (nullable): as attn_dense_bf16, over the kept keys of each row.
  *   Errors: as attn_dense_bf16, plus BAD_THRESHOLD (factor not finite or
  *   < 0). */
 int attn_skip_softmax(const void* q, const void* k, const void* v, void* o,
                       attn_dtype o_dtype, const attn_shape* shape, float sm_scale,
                       float threshold_factor, uint8_t* skip_bitmap,
-                      uint64_t* skipped_tiles, void* stream);
+                      uint64_t* skipped_tiles, float* lse, void* stream);
 
 /* Host-side timestep gate ([TA] "Skip-Softmax", key disabled_until_timestep;
  * [SSD]: host-side gate, no kernel argument).  *enabled = (t <= D), with t

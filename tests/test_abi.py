@@ -67,7 +67,7 @@ FAKE = ctypes.c_void_p(0x100000)
 
 
 def _dense(shape, o_dtype=0, scale=0.088):
-    return dit._lib().attn_dense_bf16(FAKE, FAKE, FAKE, FAKE, o_dtype, ctypes.byref(shape), scale, None)
+    return dit._lib().attn_dense_bf16(FAKE, FAKE, FAKE, FAKE, o_dtype, ctypes.byref(shape), scale, None, None)
 
 
 def test_dense_validation_codes():
@@ -84,9 +84,13 @@ def test_dense_validation_codes():
     assert _dense(_shape(S=0)) == OK               # empty problem: nothing to do
     assert _dense(_shape(Skv=0)) == INVALID        # softmax over no keys
     lib = dit._lib()
-    assert lib.attn_dense_bf16(None, FAKE, FAKE, FAKE, 0, ctypes.byref(_shape()), 0.1, None) == INVALID
-    assert lib.attn_dense_bf16(ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, 0, ctypes.byref(_shape()), 0.1, None) == LAYOUT
+    assert lib.attn_dense_bf16(None, FAKE, FAKE, FAKE, 0, ctypes.byref(_shape()), 0.1, None, None) == INVALID
+    assert lib.attn_dense_bf16(ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, 0, ctypes.byref(_shape()), 0.1, None,
+                               None) == LAYOUT
     assert b"16-byte" in lib.attn_last_error()
+    assert lib.attn_dense_bf16(FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(_shape()), 0.1, ctypes.c_void_p(0x200002),
+                               None) == LAYOUT
+    assert b"lse" in lib.attn_last_error()
 
 
 def test_valid_call_without_gpu_reports_device_error():
@@ -99,7 +103,8 @@ def test_valid_call_without_gpu_reports_device_error():
 def test_skip_threshold_validation():
     lib = dit._lib()
     for bad in (-1.0, float("nan"), float("inf")):
-        assert lib.attn_skip_softmax(FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(_shape()), 0.1, bad, None, None, None) == THRESHOLD
+        assert lib.attn_skip_softmax(FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(_shape()), 0.1, bad, None, None, None,
+                                     None) == THRESHOLD
 
 
 def _recipe(qk, qb, kb, v=3, vb=1):

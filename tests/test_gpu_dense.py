@@ -91,3 +91,35 @@ def test_empty_and_invalid_calls():
         dit.attn_dense_bf16(q, k, v)   # host tensors
     with pytest.raises(ValueError, match="mask"):
         dit.attention(qd, kd, vd, attn_mask=torch.ones(8, 8, device="cuda"))
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv", [(1, 300, 65, 4, 2), (2, 130, 513, 2, 2), (1, 1, 1, 1, 1)])
+def test_lse_matches_oracle(B, Sq, Skv, Hq, Hkv):
+    """Row log-sum-exp next to the output, for self- and cross-attention shapes."""
+    announce(f"dense lse B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}")
+    q, _, _ = gaussian_qkv(B, Sq, Hq, Hkv, seed=Sq + 5)
+    _, k, v = gaussian_qkv(B, Skv, Hq, Hkv, seed=Skv + 6, k_bias_std=2.0)
+    o, lse = dit.attn_dense_bf16(q.cuda(), k.cuda(), v.cuda(), out_dtype=torch.float32, return_lse=True)
+    o_plain = dit.attn_dense_bf16(q.cuda(), k.cuda(), v.cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, ref_lse = exact_attention(q, k, v, SC, return_lse=True)
+    dense_tolerances(to_np(o), ref)
+    assert torch.equal(o, o_plain)                       # asking for LSE changes nothing else
+    # |LSE| error: the bf16 rounding of P (relative 2^-9 per term) and fp32 sums
+    err = np.abs(to_np(lse) - ref_lse).max()
+    assert err <= 4e-3, err
+
+
+def test_lse_merges_two_key_halves():
+    """LSE-weighted merge of attention over two key halves equals attention over all keys."""
+    announce("dense lse merge")
+    q, k, v = gaussian_qkv(1, 257, 2, 2, seed=31)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = dit.attn_dense_bf16(qd, kd, vd, out_dtype=torch.float32, return_lse=True)
+    oa, la = dit.attn_dense_bf16(qd, kd[:, :100], vd[:, :100], out_dtype=torch.float32, return_lse=True)
+    ob, lb = dit.attn_dense_bf16(qd, kd[:, 100:], vd[:, 100:], out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    wa = torch.exp(la - lse).transpose(1, 2)[..., None]   # [B, Sq, Hq, 1]
+    wb = torch.exp(lb - lse).transpose(1, 2)[..., None]
+    merged = wa * oa + wb * ob
+    assert rel_l2(to_np(merged), to_np(o)) <= 5e-3

@@ -110,3 +110,18 @@ def test_wan_shape_sampled_tiles():
             r = rel_l2(to_np(o[:, rows, h:h + 1]), ref)
             assert r <= 3e-2, (factor, h, r)
         print(f"factor {factor}: skipped fraction {frac:.4f}")
+
+
+def test_lse_over_kept_keys():
+    announce("skip lse")
+    q, k, v = positional_qkv(grid=(2, 8, 24), H=2, seed=4)
+    bm, bn = dit.tile_config()
+    o, ex = dit.attn_skip_softmax(q.cuda(), k.cuda(), v.cuda(), 30.0, out_dtype=torch.float32,
+                                  return_bitmap=True, return_lse=True)
+    torch.cuda.synchronize()
+    ref, skipped, ratio, rows, ref_lse = skip_attention(q, k, v, SC, 30.0, bm, bn, return_lse=True)
+    flips = _compare_skip_sets(ex["bitmap"].cpu().numpy().astype(bool), skipped, ratio, 30.0 / q.shape[1],
+                               _log_band(q, k))[1]
+    if flips == 0:
+        err = np.abs(to_np(ex["lse"]) - ref_lse).max()
+        assert err <= 4e-3, err
