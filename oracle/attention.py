@@ -171,7 +171,9 @@ def _encode(y, dtype):
 
 
 def _decode(c, dtype):
-    return c.astype(np.float64) if dtype == "int8" else e4m3_decode(c)
+    if dtype in ("int8", "bf16"):
+        return c.astype(np.float64)
+    return e4m3_decode(c)
 
 
 def _block_quant_head(x, blk, dtype):
@@ -191,50 +193,137 @@ def _block_quant_head(x, blk, dtype):
     return _encode(y, dtype), scale
 
 
-def sage_quantize(q, k, v, qk_dtype, q_block, k_block):
-    """SAGE quantization of Q, K (smoothed) and V.
+MX_BLOCK = 32          # elements per MXFP8 scale block (along the head dimension)
+MX_EMAX_E4M3 = 8       # exponent of the largest power of two E4M3 holds (448 = 1.75 * 2**8)
 
-    * K-smoothing: K_hat = binary32(K - mu) with mu from ``k_channel_mean``;
-      Q and V are not smoothed.
-    * Q and K_hat: one scale per token block per head, blocks of ``q_block``
-      / ``k_block`` tokens along the sequence ("VisualGen Quantized
-      Attention", section "SageAttention in the TRTLLM backend"), codes int8
-      or fp8 E4M3.
-    * V: fp8 E4M3 with one scale per (batch, KV head, channel), i.e.
-      v_block_size = 1 (same section).
 
-    Returns a dict: q_codes [B,Hq,S,D], q_scale [B,Hq,ceil(S/qb)],
-    k_codes [B,Hkv,S,D], k_scale [B,Hkv,ceil(S/kb)], v_codes [B,Hkv,S,D]
-    (uint8 E4M3), v_scale [B,Hkv,D], mu [B,Hkv,D]; codes are int8 for int8
-    and uint8 E4M3 bit patterns for fp8; scales are binary32.
+def _mx_quant_rows(x):
+    """MXFP8 quantization of [S, D] binary32 rows in blocks of 32 channels.
+
+    OCP Microscaling (MX) format with E4M3 elements and an E8M0 (power of
+    two) shared scale per block: X = 2**(floor(log2(amax)) - 8), with 8 the
+    exponent of E4M3's largest normal binade, clamped to E8M0's range
+    [2**-127, 2**127] (2**-127 for an all-zero block); each element becomes
+    E4M3(x / X), rounded to nearest even and saturated at 448 (amax / X lies
+    in [256, 512)).  The division by a power of two is exact.
+    Returns (codes uint8 [S, D], exponents int [S, D / 32]).
+    """
+    S, D = x.shape
+    blocks = np.abs(x.astype(np.float64)).reshape(S, D // MX_BLOCK, MX_BLOCK)
+    amax = blocks.max(axis=2)
+    _, e = np.frexp(np.where(amax == 0, 1.0, amax))       # amax = m * 2**e, m in [0.5, 1)
+    exp = np.where(amax == 0, -127, np.clip(e - 1 - MX_EMAX_E4M3, -127, 127))
+    scale = np.ldexp(1.0, exp)
+    y = x.astype(np.float64).reshape(S, D // MX_BLOCK, MX_BLOCK) / scale[:, :, None]
+    return e4m3_encode(y.reshape(S, D)), exp.astype(np.int64)
+
+
+def sage_quantize(q, k, v, qk_dtype, q_block, k_block, v_block=1):
+    """Quantization of Q, K and V for the low-precision attention recipes.
+
+    The recipe is (qk_dtype, v_dtype = fp8, (q_block, k_block, v_block))
+    ("VisualGen Quantized Attention", section "Recipes"):
+      * SageAttention, qk_dtype int8 or fp8, blocks (1|4|16, 1|4|16, 1)
+        ("SageAttention in the TRTLLM backend"): K-smoothing
+        K_hat = binary32(K - mu) with mu from ``k_channel_mean``; Q and K_hat
+        get one scale per block of ``q_block`` / ``k_block`` tokens per head.
+      * QK16PV8, qk_dtype bf16, blocks (0, 0, 0) ("QK16PV8 Attention Kernels
+        in the CUTEDSL Backend"): Q and K stay BF16 (no scales, no smoothing).
+      * MXFP8 Q/K, qk_dtype mxfp8, blocks (0, 0, 0|1) ("MXFP8 and NVFP4 in
+        the CUTEDSL and FlashInfer backends"): Q and K in OCP MXFP8, blocks
+        of 32 channels along the head dimension (``_mx_quant_rows``); no
+        smoothing (the pages tie smoothing to SageAttention only).
+      * V: fp8 E4M3 with one scale per (batch, KV head, channel) for
+        v_block = 1, or one tensor-wide scale for v_block = 0; scale =
+        binary32(max|v| / 448) (1 if all zero).
+
+    Returns a dict: q_codes [B,Hq,S,D], k_codes [B,Hkv,S,D] (int8, uint8
+    E4M3 bits, or float32 BF16 values), q_scale / k_scale (binary32 per token
+    block [B,H,ceil(S/blk)] for SageAttention; E8M0 exponents [B,H,S,4] for
+    MXFP8; absent for BF16), v_codes [B,Hkv,S,D] (uint8 E4M3), v_scale
+    [B,Hkv,D] (binary32, all equal for v_block 0), mu [B,Hkv,D].
     """
     qf, kf, vf = _f32(q), _f32(k), _f32(v)
     B, Sq, Skv, Hq, Hkv, D = _shape_check(qf, kf, vf)
-    mu = k_channel_mean(kf)
-    cdt = np.int8 if qk_dtype == "int8" else np.uint8
+    sage = qk_dtype in ("int8", "fp8", "fp8_e4m3")
+    if sage:
+        if q_block < 1 or k_block < 1 or v_block != 1:
+            raise ValueError(f"SageAttention blocks must be (>= 1, >= 1, 1), got {(q_block, k_block, v_block)}")
+    elif qk_dtype == "bf16":
+        if (q_block, k_block, v_block) != (0, 0, 0):
+            raise ValueError("QK16PV8 takes blocks (0, 0, 0)")
+    elif qk_dtype == "mxfp8":
+        if (q_block, k_block) != (0, 0) or v_block not in (0, 1):
+            raise ValueError("MXFP8 Q/K takes blocks (0, 0, 0) or (0, 0, 1)")
+    else:
+        raise ValueError(f"unsupported qk dtype {qk_dtype!r}")
+    mu = k_channel_mean(kf) if sage else np.zeros((B, Hkv, D), np.float32)
+    cdt = {"int8": np.int8, "bf16": np.float32}.get(qk_dtype, np.uint8)
     out = {
         "q_codes": np.empty((B, Hq, Sq, D), cdt),
-        "q_scale": np.empty((B, Hq, -(-Sq // q_block)), np.float32),
         "k_codes": np.empty((B, Hkv, Skv, D), cdt),
-        "k_scale": np.empty((B, Hkv, -(-Skv // k_block)), np.float32),
         "v_codes": np.empty((B, Hkv, Skv, D), np.uint8),
         "v_scale": np.empty((B, Hkv, D), np.float32),
         "mu": mu,
-        "qk_dtype": qk_dtype, "q_block": q_block, "k_block": k_block,
+        "qk_dtype": qk_dtype, "q_block": q_block, "k_block": k_block, "v_block": v_block,
     }
-    vmax = np.float32(E4M3_MAX)
+    if sage:
+        out["q_scale"] = np.empty((B, Hq, -(-Sq // q_block)), np.float32)
+        out["k_scale"] = np.empty((B, Hkv, -(-Skv // k_block)), np.float32)
+    elif qk_dtype == "mxfp8":
+        out["q_scale"] = np.empty((B, Hq, Sq, D // MX_BLOCK), np.int64)
+        out["k_scale"] = np.empty((B, Hkv, Skv, D // MX_BLOCK), np.int64)
     for b in range(B):
         for h in range(Hq):
-            out["q_codes"][b, h], out["q_scale"][b, h] = _block_quant_head(qf[b, :, h], q_block, qk_dtype)
+            if sage:
+                out["q_codes"][b, h], out["q_scale"][b, h] = _block_quant_head(qf[b, :, h], q_block, qk_dtype)
+            elif qk_dtype == "mxfp8":
+                out["q_codes"][b, h], out["q_scale"][b, h] = _mx_quant_rows(qf[b, :, h])
+            else:
+                out["q_codes"][b, h] = qf[b, :, h]
         for g in range(Hkv):
-            khat = (kf[b, :, g] - mu[b, g][None, :]).astype(np.float32)
-            out["k_codes"][b, g], out["k_scale"][b, g] = _block_quant_head(khat, k_block, qk_dtype)
-            x = vf[b, :, g]
-            a = np.abs(x).max(axis=0)
-            sv = np.where(a == 0, np.float32(1.0), a / vmax).astype(np.float32)
-            out["v_scale"][b, g] = sv
-            out["v_codes"][b, g] = e4m3_encode((x / sv[None, :]).astype(np.float32))
+            if sage:
+                khat = (kf[b, :, g] - mu[b, g][None, :]).astype(np.float32)
+                out["k_codes"][b, g], out["k_scale"][b, g] = _block_quant_head(khat, k_block, qk_dtype)
+            elif qk_dtype == "mxfp8":
+                out["k_codes"][b, g], out["k_scale"][b, g] = _mx_quant_rows(kf[b, :, g])
+            else:
+                out["k_codes"][b, g] = kf[b, :, g]
+    vmax = np.float32(E4M3_MAX)
+    if v_block == 0:
+        a = np.float32(np.abs(vf).max()) if vf.size else np.float32(0.0)
+        out["v_scale"][...] = np.float32(1.0) if a == 0 else np.float32(a / vmax)
+    else:
+        a = np.abs(vf).max(axis=1)                                 # [B, Hkv, D]
+        out["v_scale"][...] = np.where(a == 0, np.float32(1.0), a / vmax).astype(np.float32)
+    for b in range(B):
+        for g in range(Hkv):
+            out["v_codes"][b, g] = e4m3_encode((vf[b, :, g] / out["v_scale"][b, g][None, :]).astype(np.float32))
     return out
+
+
+def _logits(quant, b, h, g, rows, keys, sm_scale):
+    """Log2-unit logits L_ij = log2(e) * sm_scale * <dequantized q_i, k_j> of
+    one (batch, query head), from the codes and scales of ``sage_quantize``:
+    sq(i) sk(j) <qc_i, kc_j> for SageAttention, the BF16 dot for QK16PV8, and
+    sum over 32-channel blocks of X_q X_k <qc, kc> for MXFP8."""
+    dt = quant["qk_dtype"]
+    qc = _decode(quant["q_codes"][b, h][rows], dt)
+    kc = _decode(quant["k_codes"][b, g][keys], dt)
+    if dt == "bf16":
+        dots = qc @ kc.T
+    elif dt == "mxfp8":
+        xq = np.ldexp(1.0, quant["q_scale"][b, h][rows])           # [R, 4]
+        xk = np.ldexp(1.0, quant["k_scale"][b, g][keys])           # [N, 4]
+        dots = np.zeros((len(rows), len(keys)))
+        for blk in range(qc.shape[1] // MX_BLOCK):
+            c = slice(MX_BLOCK * blk, MX_BLOCK * (blk + 1))
+            dots += xq[:, blk][:, None] * xk[:, blk][None, :] * (qc[:, c] @ kc[:, c].T)
+    else:
+        sq = quant["q_scale"][b, h][rows // quant["q_block"]].astype(np.float64)
+        sk = quant["k_scale"][b, g][keys // quant["k_block"]].astype(np.float64)
+        dots = sq[:, None] * sk[None, :] * (qc @ kc.T)
+    return sm_scale * dots * LOG2E
 
 
 def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale=256.0,
@@ -246,7 +335,8 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
     "SageAttention in the TRTLLM backend").  Readings taken where the pages
     are silent:
       * BMM1 scale: s_ij = sm_scale * sq(i) * sk(j) * <qc_i, kc_j>, the dot
-        exact (int8 or E4M3 codes).
+        exact (int8 or E4M3 codes); for QK16PV8 the BF16 dot, for MXFP8 the
+        sum over 32-channel blocks of X_q X_k <qc, kc> (``_logits``).
       * KV tiles of ``block_n`` keys in ascending order with an online
         softmax whose reference is a power of two: in log2 units
         L_ij = s_ij * log2(e), the reference is M = ceil(max L) over the
@@ -259,8 +349,6 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
         O_id = acc_d * sv_d / l_i.
     Returns O [B, R, Hq, D] (float64 unless ``out_dtype`` rounds it).
     """
-    dt = quant["qk_dtype"]
-    qb, kb = quant["q_block"], quant["k_block"]
     qc_all, kc_all, vc_all = quant["q_codes"], quant["k_codes"], quant["v_codes"]
     B, Hq, Sq, D = qc_all.shape
     Hkv, Skv = kc_all.shape[1], kc_all.shape[2]
@@ -271,14 +359,10 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
     keys = np.arange(Skv)
     for b in range(B):
         for g in range(Hkv):
-            kc = _decode(kc_all[b, g], dt)
-            sk = quant["k_scale"][b, g][keys // kb].astype(np.float64)
             vd = e4m3_decode(vc_all[b, g])
             sv = quant["v_scale"][b, g].astype(np.float64)
             for h in range(g * G, (g + 1) * G):
-                qc = _decode(qc_all[b, h][rows], dt)
-                sq = quant["q_scale"][b, h][rows // qb].astype(np.float64)
-                s = sm_scale * sq[:, None] * sk[None, :] * (qc @ kc.T) * LOG2E
+                s = _logits(quant, b, h, g, rows, keys, sm_scale)
                 m = np.full(R, -np.inf)
                 l = np.zeros(R)
                 acc = np.zeros((R, D))
@@ -320,8 +404,6 @@ def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, 
     skipped [B, Hq, nQT, T] bool, ratio [B, Hq, nQT, T] = max_i
     2**(M_it - m_i) with NaN at t = 0, rows).
     """
-    dt = quant["qk_dtype"]
-    qb, kb = quant["q_block"], quant["k_block"]
     qc_all, kc_all, vc_all = quant["q_codes"], quant["k_codes"], quant["v_codes"]
     B, Hq, Sq, D = qc_all.shape
     Hkv, Skv = kc_all.shape[1], kc_all.shape[2]
@@ -338,17 +420,13 @@ def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, 
     keys = np.arange(Skv)
     for b in range(B):
         for g in range(Hkv):
-            kc = _decode(kc_all[b, g], dt)
-            sk = quant["k_scale"][b, g][keys // kb].astype(np.float64)
             vd = e4m3_decode(vc_all[b, g])
             sv = quant["v_scale"][b, g].astype(np.float64)
             for h in range(g * G, (g + 1) * G):
                 r0 = 0
                 for qi, qt in enumerate(qtiles):
                     rr = np.arange(qt * block_m, min(Sq, (qt + 1) * block_m))
-                    qc = _decode(qc_all[b, h][rr], dt)
-                    sq = quant["q_scale"][b, h][rr // qb].astype(np.float64)
-                    s = sm_scale * sq[:, None] * sk[None, :] * (qc @ kc.T) * LOG2E
+                    s = _logits(quant, b, h, g, rr, keys, sm_scale)
                     m_true = np.full(len(rr), -np.inf)
                     m = np.full(len(rr), -np.inf)
                     l = np.zeros(len(rr))
