@@ -44,7 +44,7 @@ _STATUS = {
     -9: "NOT_IMPLEMENTED",
 }
 _VALIDATION = {-1, -2, -3, -4, -5, -6, -7}
-DT_BF16, DT_FP32, DT_INT8, DT_FP8 = 0, 1, 2, 3
+DT_BF16, DT_FP32, DT_INT8, DT_FP8, DT_MXFP8 = 0, 1, 2, 3, 4
 
 
 class AttnError(RuntimeError):
@@ -204,10 +204,13 @@ def attn_dense_bf16(q, k, v, out=None, out_dtype=torch.bfloat16, sm_scale=None, 
 
 @dataclass(frozen=True)
 class SageRecipe:
-    """(qk_dtype, v_dtype, (q_block, k_block, v_block)), validated like the pages' key tables.
+    """(qk_dtype, v_dtype, (q_block, k_block, v_block)), validated like the pages' recipe table.
 
-    qk_dtype: "int8" or "fp8" / "fp8_e4m3"; v_dtype: "fp8"; q_block, k_block in
-    {1, 4, 16} tokens; v_block = 1 (one V scale per head and channel).
+    SageAttention: qk_dtype "int8" or "fp8" / "fp8_e4m3", q_block, k_block in
+    {1, 4, 16} tokens, v_block = 1 (one V scale per head and channel).
+    QK16PV8: qk_dtype "bf16", blocks (0, 0, 0) (tensor-wide V scale).
+    MXFP8 Q/K: qk_dtype "mxfp8", blocks (0, 0, 0) or (0, 0, 1).
+    v_dtype is "fp8" throughout.
     """
     qk_dtype: str = "int8"
     v_dtype: str = "fp8"
@@ -216,23 +219,34 @@ class SageRecipe:
     v_block: int = 1
 
     def __post_init__(self):
-        if self.qk_dtype not in ("int8", "fp8", "fp8_e4m3"):
-            raise ValueError(f"qk_dtype must be 'int8' or 'fp8_e4m3', got {self.qk_dtype!r}")
         if self.v_dtype not in ("fp8", "fp8_e4m3"):
             raise ValueError(f"v_dtype must be 'fp8', got {self.v_dtype!r}")
-        for name in ("q_block", "k_block"):
-            if getattr(self, name) not in (1, 4, 16) or isinstance(getattr(self, name), bool):
-                raise ValueError(f"{name} must be 1, 4 or 16, got {getattr(self, name)!r}")
-        if self.v_block != 1:
-            raise ValueError("v_block must be 1 (per-channel V scale)")
+        blocks = (self.q_block, self.k_block, self.v_block)
+        if any(isinstance(x, bool) for x in blocks):
+            raise ValueError(f"block sizes must be integers, got {blocks!r}")
+        if self.qk_dtype in ("int8", "fp8", "fp8_e4m3"):
+            for name in ("q_block", "k_block"):
+                if getattr(self, name) not in (1, 4, 16):
+                    raise ValueError(f"{name} must be 1, 4 or 16, got {getattr(self, name)!r}")
+            if self.v_block != 1:
+                raise ValueError("v_block must be 1 (per-channel V scale)")
+        elif self.qk_dtype == "bf16":
+            if blocks != (0, 0, 0):
+                raise ValueError(f"the QK16PV8 recipe takes blocks (0, 0, 0), got {blocks!r}")
+        elif self.qk_dtype == "mxfp8":
+            if blocks not in ((0, 0, 0), (0, 0, 1)):
+                raise ValueError(f"the MXFP8 Q/K recipe takes blocks (0, 0, 0) or (0, 0, 1), got {blocks!r}")
+        else:
+            raise ValueError(f"qk_dtype must be 'int8', 'fp8_e4m3', 'bf16' or 'mxfp8', got {self.qk_dtype!r}")
 
     @property
     def int8(self) -> bool:
         return self.qk_dtype == "int8"
 
     def _c(self) -> _Recipe:
-        return _Recipe(qk_dtype=DT_INT8 if self.int8 else DT_FP8, v_dtype=DT_FP8,
-                       q_block=self.q_block, k_block=self.k_block, v_block=self.v_block)
+        qk = {"int8": DT_INT8, "bf16": DT_BF16, "mxfp8": DT_MXFP8}.get(self.qk_dtype, DT_FP8)
+        return _Recipe(qk_dtype=qk, v_dtype=DT_FP8, q_block=self.q_block, k_block=self.k_block,
+                       v_block=self.v_block)
 
 
 def _layout(q, k, v, recipe: SageRecipe):
@@ -276,22 +290,29 @@ def _views(ws, lay, q, k, recipe):
         return ws[off:off + nbytes].view(dtype).view(shape)
 
     cdt = torch.int8 if recipe.int8 else torch.uint8
-    return {
-        "q_codes": region(lay.q_codes_off, B * Hq * sp * D, cdt, (B, Hq, sp, D)),
-        "k_codes": region(lay.k_codes_off, B * Hkv * sp * D, cdt, (B, Hkv, sp, D)),
+    views = {
         "v_codes": region(lay.v_codes_off, B * Hkv * D * sp, torch.uint8, (B, Hkv, D, sp)),
-        "q_scale": region(lay.q_scale_off, B * Hq * lay.n_qblk, torch.float32, (B, Hq, lay.n_qblk)),
-        "k_scale": region(lay.k_scale_off, B * Hkv * lay.n_kblk, torch.float32, (B, Hkv, lay.n_kblk)),
         "v_scale": region(lay.v_scale_off, B * Hkv * D, torch.float32, (B, Hkv, D)),
         "k_mean": region(lay.k_mean_off, B * Hkv * D, torch.float32, (B, Hkv, D)),
         "s_pad": sp,
         "workspace": ws,
     }
+    if recipe.qk_dtype != "bf16":
+        views["q_codes"] = region(lay.q_codes_off, B * Hq * sp * D, cdt, (B, Hq, sp, D))
+        views["k_codes"] = region(lay.k_codes_off, B * Hkv * sp * D, cdt, (B, Hkv, sp, D))
+    if recipe.qk_dtype == "mxfp8":   # E8M0 bytes, one per 32 channels of a token
+        views["q_mx"] = region(lay.q_scale_off, B * Hq * sp * 4, torch.uint8, (B, Hq, sp, 4))
+        views["k_mx"] = region(lay.k_scale_off, B * Hkv * sp * 4, torch.uint8, (B, Hkv, sp, 4))
+    elif recipe.qk_dtype != "bf16":
+        views["q_scale"] = region(lay.q_scale_off, B * Hq * lay.n_qblk, torch.float32, (B, Hq, lay.n_qblk))
+        views["k_scale"] = region(lay.k_scale_off, B * Hkv * lay.n_kblk, torch.float32, (B, Hkv, lay.n_kblk))
+    return views
 
 
 def attn_sage(q, k, v, recipe: SageRecipe = SageRecipe(), out=None, out_dtype=torch.bfloat16,
               sm_scale=None, workspace=None):
-    """SAGE attention: quantize (K-smoothing inside) then attention on the codes."""
+    """Low-precision attention for a recipe: SageAttention (K-smoothing inside),
+    QK16PV8 or MXFP8 Q/K; quantize, then attention with an FP8 BMM2."""
     _check_tensors(q, k, v)
     out, odt = _out(q, out, out_dtype)
     lay = _layout(q, k, v, recipe)

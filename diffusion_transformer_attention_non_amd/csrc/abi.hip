@@ -167,17 +167,41 @@ int launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// The accepted recipes (qk_dtype, v_dtype, (q_block, k_block, v_block)):
+//   SageAttention  (INT8 | FP8_E4M3, FP8_E4M3, (1|4|16, 1|4|16, 1))
+//   QK16PV8        (BF16, FP8_E4M3, (0, 0, 0))
+//   MXFP8 Q/K      (MXFP8, FP8_E4M3, (0, 0, 0|1))
 int check_recipe(const attn_recipe* r) {
   if (r == nullptr) return fail(ATTN_ERR_INVALID_ARG, "recipe is NULL");
-  if (r->qk_dtype != ATTN_DTYPE_INT8 && r->qk_dtype != ATTN_DTYPE_FP8_E4M3)
-    return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "qk_dtype must be INT8 or FP8_E4M3");
   if (r->v_dtype != ATTN_DTYPE_FP8_E4M3) return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "v_dtype must be FP8_E4M3");
-  auto blk_ok = [](int b) { return b == 1 || b == 4 || b == 16; };
-  if (!blk_ok(r->q_block) || !blk_ok(r->k_block))
-    return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "q_block and k_block must be 1, 4 or 16 (got %d, %d)", r->q_block,
-                r->k_block);
-  if (r->v_block != 1) return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "v_block must be 1 (one V scale per channel)");
-  return ATTN_OK;
+  if (r->qk_dtype == ATTN_DTYPE_INT8 || r->qk_dtype == ATTN_DTYPE_FP8_E4M3) {
+    auto blk_ok = [](int b) { return b == 1 || b == 4 || b == 16; };
+    if (!blk_ok(r->q_block) || !blk_ok(r->k_block))
+      return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "q_block and k_block must be 1, 4 or 16 (got %d, %d)", r->q_block,
+                  r->k_block);
+    if (r->v_block != 1) return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "v_block must be 1 (one V scale per channel)");
+    return ATTN_OK;
+  }
+  if (r->qk_dtype == ATTN_DTYPE_BF16) {
+    if (r->q_block != 0 || r->k_block != 0 || r->v_block != 0)
+      return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "the BF16 Q/K recipe (QK16PV8) takes blocks (0, 0, 0)");
+    return ATTN_OK;
+  }
+  if (r->qk_dtype == ATTN_DTYPE_MXFP8) {
+    if (r->q_block != 0 || r->k_block != 0 || (r->v_block != 0 && r->v_block != 1))
+      return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "the MXFP8 Q/K recipe takes blocks (0, 0, 0) or (0, 0, 1)");
+    return ATTN_OK;
+  }
+  return fail(ATTN_ERR_UNSUPPORTED_RECIPE, "qk_dtype must be INT8, FP8_E4M3, BF16 or MXFP8");
+}
+
+int qk_fmt(const attn_recipe* r) {
+  switch (r->qk_dtype) {
+    case ATTN_DTYPE_INT8: return kQkInt8;
+    case ATTN_DTYPE_FP8_E4M3: return kQkFp8;
+    case ATTN_DTYPE_MXFP8: return kQkMxfp8;
+    default: return kQkBf16;
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -185,14 +209,24 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 void sage_layout(const attn_shape* s, const attn_recipe* r, attn_sage_layout* L) {
   const int64_t S = s->S_q > s->S_kv ? s->S_q : s->S_kv;
   L->s_pad = (S + kBlockN - 1) / kBlockN * kBlockN;
-  L->n_qblk = (s->S_q + r->q_block - 1) / r->q_block;
-  L->n_kblk = (s->S_kv + r->k_block - 1) / r->k_block;
+  const int fmt = qk_fmt(r);
+  if (fmt == kQkInt8 || fmt == kQkFp8) {
+    L->n_qblk = (s->S_q + r->q_block - 1) / r->q_block;
+    L->n_kblk = (s->S_kv + r->k_block - 1) / r->k_block;
+  } else if (fmt == kQkMxfp8) {   // one 4-byte word of E8M0 scales per token row
+    L->n_qblk = L->s_pad;
+    L->n_kblk = L->s_pad;
+  } else {                        // BF16 Q/K: no codes, no scales
+    L->n_qblk = 0;
+    L->n_kblk = 0;
+  }
+  const int64_t code_rows = fmt == kQkBf16 ? 0 : L->s_pad;
   const int64_t nchunks = (s->S_kv + kMeanChunk - 1) / kMeanChunk;
   size_t off = 0;
   L->q_codes_off = off;
-  off = align256(off + (size_t)(s->B * s->Hq * L->s_pad * kHeadDim));
+  off = align256(off + (size_t)(s->B * s->Hq * code_rows * kHeadDim));
   L->k_codes_off = off;
-  off = align256(off + (size_t)(s->B * s->Hkv * L->s_pad * kHeadDim));
+  off = align256(off + (size_t)(s->B * s->Hkv * code_rows * kHeadDim));
   L->v_codes_off = off;
   off = align256(off + (size_t)(s->B * s->Hkv * L->s_pad * kHeadDim));
   L->q_scale_off = off;
@@ -243,6 +277,9 @@ SageQuantArgs quant_args(const void* q, const void* k, const void* v, const attn
   a.Hq = (int)s->Hq;
   a.Hkv = (int)s->Hkv;
   a.qk_int8 = r->qk_dtype == ATTN_DTYPE_INT8;
+  a.qk_fmt = qk_fmt(r);
+  a.smooth = a.qk_fmt == kQkInt8 || a.qk_fmt == kQkFp8;
+  a.v_tensor = r->v_block == 0;
   a.q_block = r->q_block;
   a.k_block = r->k_block;
   a.s_pad = L.s_pad;
@@ -259,6 +296,8 @@ SageQuantArgs quant_args(const void* q, const void* k, const void* v, const attn
   a.k_partial = reinterpret_cast<float*>(w + L.scratch_off);
   const int64_t nchunks = (s->S_kv + kMeanChunk - 1) / kMeanChunk;
   a.v_absmax = reinterpret_cast<unsigned*>(w + align256(L.scratch_off + sizeof(float) * (size_t)(s->B * s->Hkv * nchunks * kHeadDim)));
+  a.q_mx = w + L.q_scale_off;
+  a.k_mx = w + L.k_scale_off;
   return a;
 }
 
@@ -305,6 +344,15 @@ int run_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_
   a.q_block = recipe->q_block;
   a.k_block = recipe->k_block;
   a.qk_int8 = qa.qk_int8;
+  a.qk_fmt = qa.qk_fmt;
+  a.q_mx = qa.q_mx;
+  a.k_mx = qa.k_mx;
+  a.q = q;
+  a.k = k;
+  for (int i = 0; i < 3; ++i) {
+    a.qs[i] = shape->q_stride[i];
+    a.ks[i] = shape->k_stride[i];
+  }
   a.sm_scale = sm_scale;
   a.o_fp32 = o_dtype == ATTN_DTYPE_FP32;
   unsigned long long* counter = reinterpret_cast<unsigned long long*>(skipped_tiles);

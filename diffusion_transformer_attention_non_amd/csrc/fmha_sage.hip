@@ -1,6 +1,17 @@
-// SAGE attention on quantized codes for gfx950 ("TRTLLM Attention", section
-// "SAGE quantization": both attention matmuls in low precision; "VisualGen
-// Quantized Attention", section "SageAttention in the TRTLLM backend").
+// Low-precision attention for gfx950: SageAttention on quantized codes
+// ("TRTLLM Attention", section "SAGE quantization": both attention matmuls in
+// low precision; "VisualGen Quantized Attention", section "SageAttention in
+// the TRTLLM backend"), and the recipes of the same section "Recipes" that
+// share its FP8 BMM2: QK16PV8 (BF16 Q/K, "QK16PV8 Attention Kernels in the
+// CUTEDSL Backend") and MXFP8 Q/K ("MXFP8 and NVFP4 in the CUTEDSL and
+// FlashInfer backends").
+//
+// Q/K formats (template kFmt):
+//   kFmtI8   int8 codes, one fp32 scale per token block (SageAttention);
+//   kFmtF8   OCP E4M3 codes, one fp32 scale per token block (SageAttention);
+//   kFmtMX8  OCP MXFP8: E4M3 codes with an E8M0 scale per 32 channels of a
+//            token, applied by the MFMA itself (v_mfma_scale A/B scales);
+//   kFmtBF16 Q and K read as BF16 from the inputs (QK16PV8).
 //
 // Work decomposition
 //   workgroup = 8 wavefronts = 256 query rows of one (batch, query head), two
@@ -8,10 +19,12 @@
 //   tiles of 64 keys.  While one wavefront of a SIMD issues its E4M3 MFMAs the
 //   other runs its softmax VALU work at full rate (a single wavefront issues
 //   VALU at half rate while its own E4M3 MFMA executes).  Per tile:
-//   BMM1  S^T = Kc Qc^T on int8 (v_mfma_i32_32x32x32_i8, exact int32) or
-//         OCP E4M3 (v_mfma_f32_32x32x64_f8f6f4) codes; each lane holds one
+//   BMM1  S^T = Kc Qc^T on int8 (v_mfma_i32_32x32x32_i8, exact int32), OCP
+//         E4M3 (v_mfma_scale_f32_32x32x64_f8f6f4, MXFP8 with its block
+//         scales) or BF16 (v_mfma_f32_32x32x16_bf16); each lane holds one
 //         query (lane % 32) and 32 keys of the tile; the logit in log2 units
-//         is L_ij = acc_ij * sk_j * (sq_i * sm_scale * log2 e);
+//         is L_ij = acc_ij * sk_j * (sq_i * sm_scale * log2 e), sk = sq = 1
+//         for MXFP8 and BF16;
 //   softmax with a power-of-two reference: m' = max(m, ceil(tile max of L)),
 //         P = E4M3(2^(L - m' + 8)), l += sum P (the values BMM2 multiplies);
 //   BMM2  O^T += Vc^T P^T on E4M3 codes (v_mfma_scale_f32_32x32x64_f8f6f4,
@@ -30,13 +43,21 @@
 // tile and m_i its running maximum over the tiles kept so far; lambda =
 // factor / S_kv.  The first tile is kept.
 //
-// K codes, V^T codes and the tile's 64 K scales stream into a 4-stage LDS
-// ring with buffer_load ... lds, three tiles ahead (out-of-range reads are
-// zero); one barrier per tile.  LDS layouts (16-byte chunks, XOR-swizzled so
-// that the 16 lanes an LDS cycle serves, 16 consecutive rows at one logical
-// chunk, hit 16 distinct 16-byte slots of the 64 four-byte banks):
-//   K:   64 rows x 128 B in MFMA-row order, physical chunk = logical ^ ((row >> 1) & 7);
-//   V^T: 128 rows (channel) x 64 B (keys), physical chunk = logical ^ ((row >> 2) & 3).
+// K (codes, or BF16 rows for QK16PV8), V^T codes and the tile's 64 K scale
+// words stream into a 4-stage LDS ring with buffer_load ... lds, three tiles
+// ahead (out-of-range reads are zero); one barrier per tile.  LDS layouts
+// (16-byte chunks, XOR-swizzled so that the 16 lanes an LDS cycle serves, 16
+// consecutive rows at one logical chunk, hit 16 distinct 16-byte slots of the
+// 64 four-byte banks):
+//   K codes: 64 rows x 128 B in MFMA-row order, physical chunk = logical ^ ((row >> 1) & 7);
+//   K BF16:  64 rows x 256 B in MFMA-row order, physical chunk = logical ^ (row & 15);
+//   V^T:     128 rows (channel) x 64 B (keys), physical chunk = logical ^ ((row >> 2) & 3).
+//
+// E4M3 fragments (kFmtF8, kFmtMX8): the 32x32x64 MFMA reads byte b of lane
+// half hh as k = 32 (b / 16) + 16 hh + b % 16, and its E8M0 scale for (row,
+// 32-k block g) from lane row + 32 g.  Step ks puts channels 64 ks + 32 g +
+// 16 hh + 0..15 into bytes 16 g.. of lane half hh, so hardware k block g is
+// exactly MX block 2 ks + g, whose scale the lane of half hh = g supplies.
 #include <type_traits>
 
 #include "device_common.h"
@@ -49,11 +70,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kSageWaves = kWavesPerWG;
 constexpr int kSageWaveRows = kWaveRows;   // 32 query rows per wavefront
-constexpr int kKTileB = kBlockN * kHeadDim;   // 8 KB of K codes
 constexpr int kVTileB = kHeadDim * kBlockN;   // 8 KB of V^T codes
-constexpr int kScaleOff = kKTileB + kVTileB;  // 64 fp32 K scales follow
-constexpr int kStageB = kScaleOff + kBlockN * 4;
-constexpr int kLoadsPerTile = 3;              // per wavefront: 1 K, 1 V, 1 scales
+constexpr int kLoadsPerTile = 3;              // per wavefront: K, V and scales (BF16: 2 K, 1 V)
+
+constexpr int kFmtI8 = kQkInt8, kFmtF8 = kQkFp8, kFmtMX8 = kQkMxfp8, kFmtBF16 = kQkBf16;
+// LDS stage: [K][V^T][64 K scale words] (no scales for BF16).
+template <int kFmt> constexpr int k_tile_bytes() { return kFmt == kFmtBF16 ? kBlockN * kHeadDim * 2 : kBlockN * kHeadDim; }
+template <int kFmt> constexpr int scale_off() { return k_tile_bytes<kFmt>() + kVTileB; }
+template <int kFmt> constexpr int stage_bytes() { return scale_off<kFmt>() + (kFmt == kFmtBF16 ? 0 : kBlockN * 4); }
 constexpr float kMaxRefGap = 64.0f;           // largest m - mo carried by the E8M0 P scale
 
 // s_waitcnt immediate for vmcnt(n) (lgkmcnt and expcnt left at their maxima).
@@ -74,8 +98,15 @@ __device__ __forceinline__ int sage_key_of_row(int row) {
 }
 
 // kBlock4: k_block >= 4, so each group of 4 keys (aligned) shares one K scale.
-template <bool kInt8, bool kBlock4, bool kSkip>
+template <int kFmt, bool kBlock4, bool kSkip>
 __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageArgs p) {
+  constexpr bool kInt8 = kFmt == kFmtI8;
+  constexpr bool kMx = kFmt == kFmtMX8;
+  constexpr bool kBf16 = kFmt == kFmtBF16;
+  constexpr bool kTokScales = kFmt == kFmtI8 || kFmt == kFmtF8;   // fp32 scale per token block
+  constexpr int kKTileB = k_tile_bytes<kFmt>();
+  constexpr int kScaleOff = scale_off<kFmt>();
+  constexpr int kStageB = stage_bytes<kFmt>();
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageB];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageB];
@@ -102,67 +133,126 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   const int nkt = (Skv + kBlockN - 1) / kBlockN;
   const float c = p.sm_scale * kLog2e;
 
-  // ---- Q codes of query q0 + l32, B operand of BMM1.  E4M3: 2 k-steps of
-  // 64 channels, lane half hh holds channels 64 ks + 32 hh + 0..31; int8: 4
-  // k-steps of 32, lane half holds 32 ks + 16 hh + 0..15.  K fragments use
-  // the same assignment, so the products pair matching channels.
+  // ---- Q of query q0 + l32, B operand of BMM1.  E4M3: 2 k-steps of 64
+  // channels (byte assignment above); int8: 4 k-steps of 32, lane half holds
+  // 32 ks + 16 hh + 0..15; BF16: 8 k-steps of 16, lane half holds 16 ks +
+  // 8 hh + 0..7.  K fragments use the same assignment.
   i32x8 qf8[2];
   i32x4 qi8[4];
-  float qsc;
+  bf16x8 qbf[8];
+  float qsc = c;
+  int qmx = 0;   // MXFP8: E8M0 scales of this lane's query, byte 2 ks = block 2 ks + hh
   {
-    const uint8_t* qbase = p.q_codes + ((int64_t)b * p.Hq + h) * s_pad * kHeadDim;
     const uint4 z = make_uint4(0, 0, 0, 0);
-    const int row = q0 + l32;   // rows < s_pad hold codes (zero past S_q)
-    const bool inb = row < s_pad;
-    const uint8_t* qp = qbase + (int64_t)(inb ? row : 0) * kHeadDim;
-    if constexpr (kInt8) {
+    const int row = q0 + l32;
+    if constexpr (kBf16) {
+      const bool ok = row < Sq;
+      const bf16_t* qp = static_cast<const bf16_t*>(p.q) + b * p.qs[0] + (int64_t)(ok ? row : 0) * p.qs[1] +
+                         h * p.qs[2] + 8 * hh;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qi8[ks] = __builtin_bit_cast(i32x4, inb ? ldg16(qp + 32 * ks + 16 * hh) : z);
+      for (int ks = 0; ks < 8; ++ks) qbf[ks] = __builtin_bit_cast(bf16x8, ok ? ldg16(qp + 16 * ks) : z);
     } else {
+      const uint8_t* qbase = p.q_codes + ((int64_t)b * p.Hq + h) * s_pad * kHeadDim;
+      const bool inb = row < s_pad;   // rows < s_pad hold codes (zero past S_q)
+      const uint8_t* qp = qbase + (int64_t)(inb ? row : 0) * kHeadDim;
+      if constexpr (kInt8) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint4 lo = inb ? ldg16(qp + 64 * ks + 32 * hh) : z;
-        const uint4 hi = inb ? ldg16(qp + 64 * ks + 32 * hh + 16) : z;
-        qf8[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        for (int ks = 0; ks < 4; ++ks) qi8[ks] = __builtin_bit_cast(i32x4, inb ? ldg16(qp + 32 * ks + 16 * hh) : z);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint4 lo = inb ? ldg16(qp + 64 * ks + 16 * hh) : z;
+          const uint4 hi = inb ? ldg16(qp + 64 * ks + 32 + 16 * hh) : z;
+          qf8[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+      }
+      if constexpr (kTokScales) {
+        const int qrow = row < Sq ? row : Sq - 1;
+        qsc = p.q_scale[((int64_t)b * p.Hq + h) * p.n_qblk + qrow / p.q_block] * c;
+      }
+      if constexpr (kMx) {
+        const uint32_t w = inb ? *reinterpret_cast<const uint32_t*>(p.q_mx + (((int64_t)b * p.Hq + h) * s_pad + row) * 4) : 0u;
+        qmx = (int)(w >> (8 * hh));
       }
     }
-    const int qrow = row < Sq ? row : Sq - 1;
-    qsc = p.q_scale[((int64_t)b * p.Hq + h) * p.n_qblk + qrow / p.q_block] * c;
   }
 
   // ---- Loads.  Round R (0..7) of a tile's K covers LDS rows 8R..8R+7 and
   // of its V^T rows 16R..16R+15; wavefront w issues round w of each, plus the
   // 64 scales (every wavefront writes the same 256 bytes).
-  const uint8_t* kg = p.k_codes + ((int64_t)b * p.Hkv + g) * s_pad * kHeadDim;
   const uint8_t* vg = p.v_codes + ((int64_t)b * p.Hkv + g) * kHeadDim * s_pad;
-  const float* skg = p.k_scale + ((int64_t)b * p.Hkv + g) * p.n_kblk;
-  const i32x4 krsrc = make_rsrc(kg, (uint32_t)(s_pad * kHeadDim));
   const i32x4 vrsrc = make_rsrc(vg, (uint32_t)(s_pad * kHeadDim));
-  const i32x4 srsrc = make_rsrc(skg, (uint32_t)(p.n_kblk * 4));
-  const int krow = 8 * wave + (lane >> 3);
-  const uint32_t koff = (uint32_t)(sage_key_of_row(krow) * kHeadDim + 16 * ((lane & 7) ^ ((krow >> 1) & 7)));
   const int vrow = 16 * wave + (lane >> 2);
   const uint32_t voff = (uint32_t)(vrow * s_pad + 16 * ((lane & 3) ^ ((vrow >> 2) & 3)));
-  const uint32_t soff = (uint32_t)(4 * (lane / p.k_block));
-  const uint32_t sstep = (uint32_t)(4 * (kBlockN / p.k_block));   // scale bytes per tile
   const uint32_t wave_slot = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * wave);
+  // K: codes from the workspace, or BF16 rows of the input (rows past S_kv read as zero).
+  const char* kg;
+  uint32_t kbytes, kstride_b;
+  if constexpr (kBf16) {
+    kstride_b = (uint32_t)(p.ks[1] * 2);
+    kg = reinterpret_cast<const char*>(static_cast<const bf16_t*>(p.k) + b * p.ks[0] + g * p.ks[2]);
+    kbytes = kstride_b * (uint32_t)Skv;
+  } else {
+    kstride_b = kHeadDim;
+    kg = reinterpret_cast<const char*>(p.k_codes + ((int64_t)b * p.Hkv + g) * s_pad * kHeadDim);
+    kbytes = (uint32_t)(s_pad * kHeadDim);
+  }
+  const i32x4 krsrc = make_rsrc(kg, kbytes);
+  uint32_t koff[2];
+  if constexpr (kBf16) {   // rounds i = 0, 1: LDS rows 8 wave + 4 i + lane / 16, 16-byte chunk lane % 16
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * wave + 4 * i + (lane >> 4);
+      koff[i] = (uint32_t)sage_key_of_row(r) * kstride_b + 16u * (uint32_t)((lane & 15) ^ (r & 15));
+    }
+  } else {
+    const int krow = 8 * wave + (lane >> 3);
+    koff[0] = koff[1] = (uint32_t)(sage_key_of_row(krow) * kHeadDim + 16 * ((lane & 7) ^ ((krow >> 1) & 7)));
+  }
+  // K scale words: one 4-byte word per key of the tile (fp32 scale of its
+  // token block, or its four MXFP8 E8M0 bytes).
+  i32x4 srsrc = {0, 0, 0, 0};
+  uint32_t soff = 0, sstep = 0;
+  if constexpr (kTokScales) {
+    const float* skg = p.k_scale + ((int64_t)b * p.Hkv + g) * p.n_kblk;
+    srsrc = make_rsrc(skg, (uint32_t)(p.n_kblk * 4));
+    soff = (uint32_t)(4 * (lane / p.k_block));
+    sstep = (uint32_t)(4 * (kBlockN / p.k_block));
+  } else if constexpr (kMx) {
+    srsrc = make_rsrc(p.k_mx + ((int64_t)b * p.Hkv + g) * s_pad * 4, (uint32_t)(s_pad * 4));
+    soff = (uint32_t)(4 * lane);
+    sstep = (uint32_t)(4 * kBlockN);
+  }
   auto issue_loads = [&](uint32_t sbase, int t) __attribute__((always_inline)) {
-    buffer_load_lds16(krsrc, sbase + wave_slot, koff + (uint32_t)t * kKTileB);
+    if constexpr (kBf16) {
+      const uint32_t tk = (uint32_t)t * kBlockN * kstride_b;
+      buffer_load_lds16(krsrc, sbase + 2 * wave_slot, koff[0] + tk);
+      buffer_load_lds16(krsrc, sbase + 2 * wave_slot + 1024, koff[1] + tk);
+    } else {
+      buffer_load_lds16(krsrc, sbase + wave_slot, koff[0] + (uint32_t)t * kKTileB);
+    }
     buffer_load_lds16(vrsrc, sbase + kKTileB + wave_slot, voff + (uint32_t)t * kBlockN);
-    buffer_load_lds4(srsrc, sbase + kScaleOff, soff + (uint32_t)t * sstep);
+    if constexpr (!kBf16) buffer_load_lds4(srsrc, sbase + kScaleOff, soff + (uint32_t)t * sstep);
   };
 
   // ---- LDS read addresses (lane constants; the rest is immediate).
   //   K: E4M3 fragment (kb, ks) = row 32 kb + l32, logical chunks 4 ks + 2 hh + e;
   //      int8 fragment (kb, ks) = logical chunk 2 ks + hh.
   //   V^T: fragment db = row 32 db + l32, logical chunks 2 hh + e.
-  int ka[4], va[2];
+  int ka[8], va[2];
   {
-    const int f = (l32 >> 1) & 7;
+    if constexpr (kBf16) {   // fragment ks: row 32 kb + l32, logical chunk 2 ks + hh
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lc = kInt8 ? 2 * i + hh : 4 * (i >> 1) + 2 * hh + (i & 1);
-      ka[i] = l32 * kHeadDim + 16 * (lc ^ f);
+      for (int i = 0; i < 8; ++i) ka[i] = l32 * 2 * kHeadDim + 16 * ((2 * i + hh) ^ (l32 & 15));
+    } else {
+      const int f = (l32 >> 1) & 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {   // int8: chunk 2 i + hh; E4M3: chunk 4 (i / 2) + 2 (i % 2) + hh
+        const int lc = kInt8 ? 2 * i + hh : 4 * (i >> 1) + 2 * (i & 1) + hh;
+        ka[i] = l32 * kHeadDim + 16 * (lc ^ f);
+      }
+#pragma unroll
+      for (int i = 4; i < 8; ++i) ka[i] = 0;
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) va[e] = kKTileB + l32 * kBlockN + 16 * ((2 * hh + e) ^ ((l32 >> 2) & 3));
@@ -199,7 +289,19 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   // BMM1 of the tile in stage sm into s: S^T of keys 32 hh + 16 kb + r
   // (register r of block kb); int8 accumulators are converted to float.
   auto bmm1 = [&](const uint8_t* sm, f32x16 (&s)[2]) __attribute__((always_inline)) {
-    if constexpr (kInt8) {
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm + ka[ks] + kb * 32 * 2 * kHeadDim);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qbf[ks], s[kb], 0, 0, 0);
+        }
+    } else if constexpr (kInt8) {
       i32x16 acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -221,6 +323,13 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      int kmx[2] = {0, 0};   // MXFP8: E8M0 scales of this lane's key row, byte 2 ks = block 2 ks + hh
+      if constexpr (kMx) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          kmx[kb] = (int)(*reinterpret_cast<const uint32_t*>(sm + kScaleOff + 4 * sage_key_of_row(32 * kb + l32)) >>
+                          (8 * hh));
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -228,15 +337,22 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
           const i32x4 lo = *reinterpret_cast<const i32x4*>(sm + ka[2 * ks] + kb * 32 * kHeadDim);
           const i32x4 hi = *reinterpret_cast<const i32x4*>(sm + ka[2 * ks + 1] + kb * 32 * kHeadDim);
           const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[ks], s[kb], 0, 0, 0, 0, 0, 0);
+          if constexpr (kMx) {
+            if (ks == 0)
+              s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[0], s[kb], 0, 0, 0, kmx[kb], 0, qmx);
+            else
+              s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[1], s[kb], 0, 0, 2, kmx[kb], 2, qmx);
+          } else {
+            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[ks], s[kb], 0, 0, 0, 0, 0, 0);
+          }
         }
     }
   };
   // Softmax of S(tile) (keys key0..key0+63, scales and V^T in stage sm), then BMM2.
   auto softmax_bmm2 = [&](const uint8_t* sm, f32x16 (&s)[2], int key0) __attribute__((always_inline)) {
-    // Dequantization (K scale per key), tail mask, row maximum.
+    // Dequantization (K scale per key; SageAttention only), tail mask, row maximum.
 #pragma unroll
-    for (int gq = 0; gq < 8; ++gq) {
+    for (int gq = 0; gq < 8 && kTokScales; ++gq) {
       const int kb = gq >> 2, r0 = 4 * (gq & 3);
       f32x4 sk;
       if constexpr (kBlock4) {
@@ -378,6 +494,14 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   }
 }
 
+template <int kFmt, bool kBlock4>
+void launch_fmt(const FmhaSageArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (a.skip)
+    hipLaunchKernelGGL((fmha_sage_kernel<kFmt, kBlock4, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fmha_sage_kernel<kFmt, kBlock4, false>), grid, block, 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_fmha_sage(const FmhaSageArgs& a, hipStream_t stream) {
@@ -386,20 +510,18 @@ hipError_t launch_fmha_sage(const FmhaSageArgs& a, hipStream_t stream) {
   if (nwg <= 0) return hipSuccess;
   const dim3 grid((unsigned)nwg), block(kSageWaves * 64);
   const bool b4 = a.k_block % 4 == 0;
-  if (a.skip) {
-    if (a.qk_int8) {
-      if (b4) hipLaunchKernelGGL((fmha_sage_kernel<true, true, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((fmha_sage_kernel<true, false, true>), grid, block, 0, stream, a);
-    } else {
-      if (b4) hipLaunchKernelGGL((fmha_sage_kernel<false, true, true>), grid, block, 0, stream, a);
-      else hipLaunchKernelGGL((fmha_sage_kernel<false, false, true>), grid, block, 0, stream, a);
-    }
-  } else if (a.qk_int8) {
-    if (b4) hipLaunchKernelGGL((fmha_sage_kernel<true, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fmha_sage_kernel<true, false, false>), grid, block, 0, stream, a);
-  } else {
-    if (b4) hipLaunchKernelGGL((fmha_sage_kernel<false, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((fmha_sage_kernel<false, false, false>), grid, block, 0, stream, a);
+  switch (a.qk_fmt) {
+    case kFmtI8:
+      if (b4) launch_fmt<kFmtI8, true>(a, grid, block, stream);
+      else launch_fmt<kFmtI8, false>(a, grid, block, stream);
+      break;
+    case kFmtF8:
+      if (b4) launch_fmt<kFmtF8, true>(a, grid, block, stream);
+      else launch_fmt<kFmtF8, false>(a, grid, block, stream);
+      break;
+    case kFmtMX8: launch_fmt<kFmtMX8, false>(a, grid, block, stream); break;
+    case kFmtBF16: launch_fmt<kFmtBF16, false>(a, grid, block, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

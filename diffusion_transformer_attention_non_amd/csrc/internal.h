@@ -36,13 +36,19 @@ hipError_t launch_fmha_bf16_skip(const FmhaBf16Args& a, hipStream_t stream);   /
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
 hipError_t launch_fill_u8(uint8_t* p, size_t n, uint8_t value, hipStream_t stream);
 
+// Q/K formats of the low-precision attention path.
+constexpr int kQkInt8 = 0, kQkFp8 = 1, kQkMxfp8 = 2, kQkBf16 = 3;
+
 struct SageQuantArgs {
   const void* q;
   const void* k;
   const void* v;
   int64_t qs[3], ks[3], vs[3];
   int B, Sq, Skv, Hq, Hkv;
-  int qk_int8;          // 1 = int8 codes, 0 = E4M3 codes
+  int qk_int8;          // 1 = int8 codes, 0 = E4M3 codes (token-block scales)
+  int qk_fmt;           // kQk*
+  int smooth;           // 1 = K-smoothing (SageAttention recipes)
+  int v_tensor;         // 1 = one tensor-wide V scale, 0 = one per (b, kv head, channel)
   int q_block, k_block;
   int64_t s_pad, n_qblk, n_kblk;
   uint8_t* q_codes;     // [B, Hq, s_pad, 128]
@@ -54,6 +60,8 @@ struct SageQuantArgs {
   float* k_mean;        // [B, Hkv, 128]
   float* k_partial;     // [B, Hkv, n_chunks, 128]
   unsigned* v_absmax;   // [B, Hkv, 128] float bits
+  uint8_t* q_mx;        // MXFP8: [B, Hq, s_pad, 4] E8M0 bytes (aliases q_scale's region)
+  uint8_t* k_mx;        // MXFP8: [B, Hkv, s_pad, 4]
 };
 
 hipError_t launch_sage_quantize(const SageQuantArgs& a, hipStream_t stream);
@@ -65,6 +73,12 @@ struct FmhaSageArgs {
   const float* q_scale;
   const float* k_scale;
   const float* v_scale;
+  const uint8_t* q_mx;    // MXFP8 E8M0 bytes [B, Hq, s_pad, 4]
+  const uint8_t* k_mx;    // [B, Hkv, s_pad, 4]
+  const void* q;          // BF16 Q and K (QK16PV8), element strides (b, s, h)
+  const void* k;
+  int64_t qs[3], ks[3];
+  int qk_fmt;             // kQk*
   void* o;
   int64_t os[3];
   int B, Sq, Skv, Hq, Hkv;

@@ -1,9 +1,11 @@
-// SAGE quantization kernels for gfx950: K-smoothing mean, per-block Q/K
-// codes, per-channel E4M3 V codes ("TRTLLM Attention", section "SAGE
-// quantization"; "VisualGen Quantized Attention", section "SageAttention in
-// the TRTLLM backend").  All of these are HBM-bound streaming kernels.
+// Quantization kernels for gfx950: K-smoothing mean, per-block Q/K codes,
+// per-channel E4M3 V codes ("TRTLLM Attention", section "SAGE quantization";
+// "VisualGen Quantized Attention", section "SageAttention in the TRTLLM
+// backend"), and for the other recipes of that page's section "Recipes"
+// MXFP8 Q/K codes with E8M0 block scales and a tensor-wide V scale.  All of
+// these are HBM-bound streaming kernels.
 //
-// Pipeline (one stream, three launches):
+// Pipeline (one stream, three launches; QK16PV8 quantizes V only):
 //   1. kv_stats:  per (b, kv head, 256-token chunk, channel) the binary32 sum of
 //                 K over the chunk in ascending token order, and max |V| per
 //                 (b, kv head, channel) via an integer atomic max on the float
@@ -11,8 +13,11 @@
 //   2. kv_finish: mu = (sum of the chunk sums in ascending chunk order) / S_kv
 //                 and the V scale max|V| / 448 (1 when the channel is all zero).
 //   3. quantize:  Q and K_hat = K - mu per token block (absmax reduced across
-//                 lanes), and V per channel written transposed (d-major), the
-//                 layout the attention kernel reads as the BMM2 A operand.
+//                 lanes), or Q and K in MXFP8 (32-channel blocks), and V
+//                 written transposed (d-major), the layout the attention
+//                 kernel reads as the BMM2 A operand.
+// Without K-smoothing (MXFP8, QK16PV8) mu is 0 and K is not summed; with a
+// tensor-wide V scale one more launch reduces the channel maxima.
 // Divisions are correctly rounded binary32 (the default HIP division); the
 // E4M3 conversion is the hardware v_cvt_pk_fp8_f32 (OCP E4M3, round to
 // nearest even, subnormals kept) applied after clamping to +-448, which makes
@@ -63,13 +68,14 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(SageQuantArgs a) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float vmax[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int s_end = min(a.Skv, (c + 1) * kMeanChunk);
+  const bool smooth = a.smooth != 0;
   for (int s = c * kMeanChunk; s < s_end; ++s) {
     float kx[8], vx[8];
-    unpack8(ldg16(kp + (int64_t)s * a.ks[1]), kx);
+    if (smooth) unpack8(ldg16(kp + (int64_t)s * a.ks[1]), kx);
     unpack8(ldg16(vp + (int64_t)s * a.vs[1]), vx);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      acc[j] = acc[j] + kx[j];
+      if (smooth) acc[j] = acc[j] + kx[j];
       vmax[j] = fmaxf(vmax[j], fabsf(vx[j]));
     }
   }
@@ -95,9 +101,71 @@ __global__ __launch_bounds__(128) void kv_finish_kernel(SageQuantArgs a) {
   float tot = 0.0f;
   for (int c = 0; c < nchunks; ++c) tot = tot + part[(int64_t)c * kHeadDim];
   const int64_t idx = ((int64_t)b * a.Hkv + g) * kHeadDim + d;
-  a.k_mean[idx] = tot / (float)a.Skv;
+  a.k_mean[idx] = a.smooth ? tot / (float)a.Skv : 0.0f;
   const float vmax = __uint_as_float(a.v_absmax[idx]);
   a.v_scale[idx] = vmax == 0.0f ? 1.0f : vmax / kE4M3Max;
+}
+
+// Tensor-wide V scale: max over every channel maximum (one workgroup), then
+// the same scale max / 448 in every v_scale entry.
+__global__ __launch_bounds__(1024) void v_tensor_scale_kernel(SageQuantArgs a) {
+  __shared__ unsigned red[1024];
+  const int n = a.B * a.Hkv * kHeadDim;
+  unsigned m = 0u;
+  for (int i = threadIdx.x; i < n; i += 1024) m = max(m, a.v_absmax[i]);   // non-negative floats order as integers
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const float vmax = __uint_as_float(red[0]);
+  const float scale = vmax == 0.0f ? 1.0f : vmax / kE4M3Max;
+  for (int i = threadIdx.x; i < n; i += 1024) a.v_scale[i] = scale;
+}
+
+// MXFP8 Q/K: OCP MX with E4M3 elements, one E8M0 scale per 32 channels of a
+// token.  Thread (row 16 wave-groups..): 16 lanes per token row, 8 channels
+// per lane, 4 lanes per 32-channel block.  X = 2^e with e = floor(log2 amax)
+// - 8 (8: exponent of E4M3's largest binade), clamped to [-127, 127]
+// (-127 for an all-zero block); code = E4M3(x / X) saturated at 448.  The
+// E8M0 byte is e + 127.  Rows past S (up to s_pad) get zero codes and byte 0.
+__global__ __launch_bounds__(256) void mx_quant_kernel(SageQuantArgs a) {
+  const int head = blockIdx.y, b = blockIdx.z;
+  const bool is_q = head < a.Hq;
+  const int hh = is_q ? head : head - a.Hq;
+  const int S = is_q ? a.Sq : a.Skv;
+  const int64_t* st = is_q ? a.qs : a.ks;
+  const bf16_t* src = static_cast<const bf16_t*>(is_q ? a.q : a.k) + b * st[0] + hh * st[2];
+  const int H = is_q ? a.Hq : a.Hkv;
+  uint8_t* codes = (is_q ? a.q_codes : a.k_codes) + ((int64_t)b * H + hh) * a.s_pad * kHeadDim;
+  uint8_t* mx = (is_q ? a.q_mx : a.k_mx) + ((int64_t)b * H + hh) * a.s_pad * 4;
+  const int s = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (s >= a.s_pad) return;
+  const int d0 = 8 * (threadIdx.x & 15);
+  float x[8];
+  if (s < S) {
+    unpack8(ldg16(src + (int64_t)s * st[1] + d0), x);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = 0.0f;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+  am = fmaxf(am, __shfl_xor(am, 1, 64));
+  am = fmaxf(am, __shfl_xor(am, 2, 64));
+  // floor(log2 am) from the binary32 exponent field (a subnormal am is below
+  // 2^-126, where the clamp to -127 applies anyway).
+  const int ebits = (int)((__float_as_uint(am) >> 23) & 0xFF);
+  int e = ebits - 127 - 8;
+  e = am == 0.0f ? -127 : (e < -127 ? -127 : (e > 127 ? 127 : e));
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact (e <= 126 here)
+  uint32_t w0, w1;
+  w0 = e4m3_pair(x[0] * inv, x[1] * inv) | e4m3_pair(x[2] * inv, x[3] * inv) << 16;
+  w1 = e4m3_pair(x[4] * inv, x[5] * inv) | e4m3_pair(x[6] * inv, x[7] * inv) << 16;
+  *reinterpret_cast<uint2*>(codes + (int64_t)s * kHeadDim + d0) = make_uint2(w0, w1);
+  if ((threadIdx.x & 3) == 0) mx[(int64_t)s * 4 + ((threadIdx.x & 15) >> 2)] = (uint8_t)(e + 127);
 }
 
 // Q / K_hat block quantization.  One wavefront per 16-token group of one
@@ -246,11 +314,14 @@ hipError_t launch_sage_quantize(const SageQuantArgs& a, hipStream_t stream) {
                        stream, a);
   }
   hipLaunchKernelGGL(kv_finish_kernel, dim3(a.Hkv, a.B), dim3(128), 0, stream, a);
+  if (a.v_tensor) hipLaunchKernelGGL(v_tensor_scale_kernel, dim3(1), dim3(1024), 0, stream, a);
   const unsigned groups = (unsigned)((a.s_pad / 16 + 3) / 4);
-  if (a.qk_int8)
+  if (a.qk_fmt == kQkInt8)
     hipLaunchKernelGGL(qk_quant_kernel<true>, dim3(groups, a.Hq + a.Hkv, a.B), dim3(256), 0, stream, a);
-  else
+  else if (a.qk_fmt == kQkFp8)
     hipLaunchKernelGGL(qk_quant_kernel<false>, dim3(groups, a.Hq + a.Hkv, a.B), dim3(256), 0, stream, a);
+  else if (a.qk_fmt == kQkMxfp8)
+    hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)(a.s_pad / 16), a.Hq + a.Hkv, a.B), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(v_quant_kernel, dim3((unsigned)(a.s_pad / 64), a.Hkv, a.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

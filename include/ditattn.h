@@ -64,7 +64,8 @@ typedef enum {
   ATTN_DTYPE_BF16 = 0,
   ATTN_DTYPE_FP32 = 1,
   ATTN_DTYPE_INT8 = 2,
-  ATTN_DTYPE_FP8_E4M3 = 3             /* OCP OFP8 E4M3 */
+  ATTN_DTYPE_FP8_E4M3 = 3,            /* OCP OFP8 E4M3 */
+  ATTN_DTYPE_MXFP8 = 4                /* OCP MX: E4M3 elements, E8M0 scale per 32 */
 } attn_dtype;
 
 /* Problem shape and strides (in elements).  stride[0..2] = b, s, h. */
@@ -76,9 +77,19 @@ typedef struct {
   int64_t o_stride[3];
 } attn_shape;
 
-/* SAGE recipe ([VQA] "Recipes"): qk_dtype in {INT8, FP8_E4M3}, v_dtype =
- * FP8_E4M3, q_block and k_block in {1, 4, 16} tokens ([TA], [DAB] key tables),
- * v_block = 1 (one V scale per head per channel, [VQA]). */
+/* Low-precision attention recipe ([VQA] "Recipes": the tuple (qk_dtype,
+ * v_dtype, (q_block, k_block, v_block))).  Accepted:
+ *   SageAttention  qk_dtype INT8 or FP8_E4M3, q_block and k_block in
+ *                  {1, 4, 16} tokens ([TA], [DAB] key tables), v_block = 1
+ *                  (one V scale per head per channel, [VQA]);
+ *   QK16PV8        qk_dtype BF16, blocks (0, 0, 0): Q/K stay BF16, V in
+ *                  E4M3 with one tensor-wide scale ([VQA] "QK16PV8 Attention
+ *                  Kernels in the CUTEDSL Backend");
+ *   MXFP8 Q/K      qk_dtype MXFP8, blocks (0, 0, 0) or (0, 0, 1): Q/K in OCP
+ *                  MXFP8 along the head dimension, V in E4M3 with a
+ *                  tensor-wide (0) or per-channel (1) scale ([VQA] "MXFP8
+ *                  and NVFP4 in the CUTEDSL and FlashInfer backends").
+ * v_dtype is FP8_E4M3 for all. */
 typedef struct {
   attn_dtype qk_dtype;
   attn_dtype v_dtype;
@@ -94,9 +105,15 @@ typedef struct {
  *   v_codes  [B, Hkv, 128, s_pad]  E4M3 bytes, transposed (d-major)
  *   q_scale  [B, Hq,  n_qblk]      fp32, n_qblk = ceil(S_q / q_block)
  *   k_scale  [B, Hkv, n_kblk]      fp32, n_kblk = ceil(S_kv / k_block)
- *   v_scale  [B, Hkv, 128]         fp32
- *   k_mean   [B, Hkv, 128]         fp32 (the K-smoothing mean)
- * s_pad is max(S_q, S_kv) rounded up to a multiple of 64. */
+ *   v_scale  [B, Hkv, 128]         fp32 (all equal for a tensor-wide scale)
+ *   k_mean   [B, Hkv, 128]         fp32 (the K-smoothing mean; 0 when the
+ *                                  recipe does not smooth)
+ * s_pad is max(S_q, S_kv) rounded up to a multiple of 64.  MXFP8: q_codes
+ * and k_codes hold E4M3 codes of Q and K (no smoothing), and the q_scale /
+ * k_scale regions hold [B, H, s_pad, 4] E8M0 bytes (byte c scales channels
+ * 32 c..32 c + 31 by 2^(byte - 127); n_qblk = n_kblk = s_pad).  BF16
+ * (QK16PV8): the code and scale regions of Q and K are empty (n_qblk =
+ * n_kblk = 0). */
 typedef struct {
   size_t total_bytes;
   size_t q_codes_off, k_codes_off, v_codes_off;

@@ -13,6 +13,7 @@ from diffusion_transformer_attention_non_amd import _Layout, _Recipe, _Shape
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ditattn.h")
 GOLDEN_RECIPES = os.path.join(ROOT, "tests", "golden", "trtllm_sage_recipes.txt")
+GOLDEN_CUTEDSL = os.path.join(ROOT, "tests", "golden", "cutedsl_recipes.txt")
 
 OK, INVALID, HEAD_DIM, GQA, RECIPE, LAYOUT, THRESHOLD, WS, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
@@ -135,14 +136,35 @@ def test_recipes_listed_on_the_pages_are_accepted():
                 assert _layout(_shape(), _recipe(qk, qb, kb))[0] == OK
 
 
+def test_bf16_and_mxfp8_recipes_listed_on_the_pages_are_accepted():
+    names = {"bf16": 0, "mxfp8": 4, "fp8": 3}
+    n = 0
+    for line in open(GOLDEN_CUTEDSL):
+        if line.startswith("#") or not line.strip():
+            continue
+        qk, v, qb, kb, vb = line.split()
+        rc, lay = _layout(_shape(S=300), _recipe(names[qk], int(qb), int(kb), names[v], int(vb)))
+        assert rc == OK, line
+        dit.SageRecipe(qk, v, int(qb), int(kb), int(vb))
+        if qk == "bf16":      # no Q/K codes or scales
+            assert lay.n_qblk == 0 and lay.k_codes_off == lay.q_codes_off and lay.v_codes_off == lay.k_codes_off
+        else:                 # one 4-byte word of E8M0 scales per token row
+            assert lay.n_qblk == lay.s_pad == 320 and lay.n_kblk == 320
+        n += 1
+    assert n == 3
+
+
 @pytest.mark.parametrize("qk,qb,kb,v,vb", [(0, 1, 16, 3, 1), (1, 1, 16, 3, 1), (2, 2, 16, 3, 1), (2, 1, 8, 3, 1),
-                                           (3, 1, 32, 3, 1), (2, 1, 16, 2, 1), (2, 1, 16, 3, 0), (2, 0, 16, 3, 1)])
+                                           (3, 1, 32, 3, 1), (2, 1, 16, 2, 1), (2, 1, 16, 3, 0), (2, 0, 16, 3, 1),
+                                           (0, 0, 0, 3, 1), (4, 0, 0, 3, 2), (4, 1, 0, 3, 0), (4, 0, 0, 4, 0),
+                                           (5, 0, 0, 3, 0)])
 def test_other_recipes_are_rejected(qk, qb, kb, v, vb):
     assert _layout(_shape(), _recipe(qk, qb, kb, v, vb))[0] == RECIPE
 
 
 @pytest.mark.parametrize("kw", [dict(qk_dtype="int4"), dict(v_dtype="int8"), dict(q_block=2), dict(k_block=32),
-                                dict(v_block=0), dict(q_block=True)])
+                                dict(v_block=0), dict(q_block=True), dict(qk_dtype="bf16"),
+                                dict(qk_dtype="mxfp8", q_block=0, k_block=0, v_block=2)])
 def test_python_recipe_validation(kw):
     with pytest.raises(ValueError):
         dit.SageRecipe(**kw)

@@ -1,0 +1,100 @@
+"""QK16PV8 and MXFP8 Q/K recipes on the GPU: quantizer bit-exact against the
+oracle, attention against the oracle's tile-ordered emulation."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_non_amd as dit
+from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate, positional_qkv
+from oracle import exact_attention, sage_attention, sage_quantize, sage_skip_attention
+from tests._gpu_util import announce, needs_gpu, rel_l2, to_np
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+SC = 1 / math.sqrt(128)
+RECIPES = [("bf16", 0, 0, 0), ("mxfp8", 0, 0, 0), ("mxfp8", 0, 0, 1)]
+
+
+def _check_quant(gpu, ref, S_q, S_kv, dt):
+    vc = gpu["v_codes"].cpu().numpy()
+    assert np.array_equal(vc[:, :, :, :S_kv].transpose(0, 1, 3, 2), ref["v_codes"])
+    assert not vc[:, :, :, S_kv:].any()
+    assert np.array_equal(gpu["v_scale"].cpu().numpy(), ref["v_scale"])
+    assert not gpu["k_mean"].cpu().numpy().any()
+    if dt == "mxfp8":
+        qc, kc = gpu["q_codes"].cpu().numpy(), gpu["k_codes"].cpu().numpy()
+        assert np.array_equal(qc[:, :, :S_q], ref["q_codes"]) and np.array_equal(kc[:, :, :S_kv], ref["k_codes"])
+        assert not qc[:, :, S_q:].any() and not kc[:, :, S_kv:].any()
+        qm = gpu["q_mx"].cpu().numpy().astype(np.int64) - 127
+        km = gpu["k_mx"].cpu().numpy().astype(np.int64) - 127
+        assert np.array_equal(qm[:, :, :S_q], ref["q_scale"]) and np.array_equal(km[:, :, :S_kv], ref["k_scale"])
+
+
+@pytest.mark.parametrize("rec", RECIPES)
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv", [(1, 300, 300, 2, 2), (2, 130, 257, 4, 2), (1, 17, 70, 1, 1)])
+def test_quantizer_bit_exact(rec, B, Sq, Skv, Hq, Hkv):
+    announce(f"quantize {rec} B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}")
+    q, _, _ = gaussian_qkv(B, Sq, Hq, Hkv, seed=Sq + 1)
+    _, k, v = gaussian_qkv(B, Skv, Hq, Hkv, seed=Skv + 2, k_bias_std=4.0, outliers=4)
+    q = q * torch.exp(torch.linspace(-6, 6, 128)).to(torch.bfloat16)     # channel blocks of very different size
+    r = dit.SageRecipe(rec[0], "fp8", *rec[1:])
+    gpu = dit.sage_quantize(q.cuda(), k.cuda(), v.cuda(), r)
+    torch.cuda.synchronize()
+    _check_quant(gpu, sage_quantize(q, k, v, *rec), Sq, Skv, rec[0])
+
+
+@pytest.mark.parametrize("rec", RECIPES)
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv", [(1, 300, 300, 2, 2), (2, 130, 257, 4, 2), (1, 1, 70, 1, 1)])
+def test_attention_matches_emulation(rec, B, Sq, Skv, Hq, Hkv):
+    announce(f"attention {rec} B={B} Sq={Sq} Skv={Skv} Hq={Hq} Hkv={Hkv}")
+    q, _, _ = gaussian_qkv(B, Sq, Hq, Hkv, seed=Sq)
+    _, k, v = gaussian_qkv(B, Skv, Hq, Hkv, seed=Skv + 1, k_bias_std=4.0, outliers=4)
+    r = dit.SageRecipe(rec[0], "fp8", *rec[1:])
+    o = dit.attn_sage(q.cuda(), k.cuda(), v.cuda(), r, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    emu = sage_attention(sage_quantize(q, k, v, *rec), SC, dit.kv_tile())
+    rr = rel_l2(to_np(o), emu)
+    assert rr <= 5e-3, rr
+    # sanity against unquantized attention; MXFP8 does not smooth K, so the
+    # K bias of these inputs (std 4, outlier channels x8) costs it accuracy
+    bar = 0.1 if rec[0] == "bf16" else 0.3
+    assert rel_l2(to_np(o), exact_attention(q, k, v, SC)) <= bar
+
+
+@pytest.mark.parametrize("rec", [("bf16", 0, 0, 0), ("mxfp8", 0, 0, 1)])
+def test_skip_softmax_with_recipe_matches_oracle(rec):
+    announce(f"skip {rec}")
+    q, k, v = positional_qkv(grid=(2, 8, 24), H=2, seed=2)
+    r = dit.SageRecipe(rec[0], "fp8", *rec[1:])
+    o, ex = dit.attn_sage_skip_softmax(q.cuda(), k.cuda(), v.cuda(), r, 10.0, out_dtype=torch.float32,
+                                       return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    quant = sage_quantize(q, k, v, *rec)
+    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 10.0, dit.tile_config()[0], dit.kv_tile())
+    got = ex["bitmap"].cpu().numpy().astype(bool)
+    lam = 10.0 / q.shape[1]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        near = np.abs(np.log2(ratio) - math.log2(lam)) <= 1e-4
+    assert not ((got != skipped) & ~near).any()
+    assert skipped.any() and int(ex["skipped"][0]) == int(got.sum())
+    r_ = rel_l2(to_np(o)[:, rows], ref)
+    assert r_ <= 3e-2 and (((got != skipped) & near).any() or r_ <= 5e-3), r_
+
+
+def test_mxfp8_wan_shape_sampled():
+    """B=1, H=40, S=75,600 Gaussian inputs with K bias and outlier channels, MXFP8 Q/K, per-channel V; sampled rows."""
+    announce("mxfp8 wan generate")
+    qd, kd, vd = generate("sage_fp8_wan_b1_h40_s75600", device="cuda")
+    r = dit.SageRecipe("mxfp8", "fp8", 0, 0, 1)
+    announce("mxfp8 wan attention")
+    o = dit.attn_sage(qd, kd, vd, r)
+    torch.cuda.synchronize()
+    q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
+    rows = np.concatenate([np.arange(0, 32), np.arange(40000, 40032), np.arange(75568, 75600)])
+    for h in (0, 39):
+        sl = slice(h, h + 1)
+        quant = sage_quantize(q[:, :, sl], k[:, :, sl], v[:, :, sl], "mxfp8", 0, 0, 1)
+        emu = sage_attention(quant, SC, dit.kv_tile(), rows=rows)
+        rr = rel_l2(to_np(o[:, rows, sl]), emu)
+        assert rr <= 3e-2, (h, rr)
