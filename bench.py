@@ -269,6 +269,16 @@ def main():
             sweep[str(f)] = {"ms": ms, "effective_tflops": F / ms / 1e9, "skip_fraction": frac,
                              "algorithmic_tflops": (2 + 2 * (1 - frac)) * B * H * S * S * D / ms / 1e9}
         extra["sage_fp8_skip_factor_sweep_wan"] = sweep
+        # The other FP8-BMM2 recipes at the same shape, on the SAGE workload's
+        # inputs (quantization included): QK16PV8 and MXFP8 Q/K.
+        for name, r in (("qk16pv8_bf16_000", dit.SageRecipe("bf16", "fp8", 0, 0, 0)),
+                        ("mxfp8_001", dit.SageRecipe("mxfp8", "fp8", 0, 0, 1))):
+            wsr = dit.sage_workspace(q4, k4, v4, r)
+            ms = timed_calls(lambda: dit.attn_sage(q4, k4, v4, r, out=o_sage, workspace=wsr), 3, torch)
+            peak = PEAK_TFLOPS["fp8"] if r.qk_dtype == "mxfp8" else 1.0 / (0.5 / PEAK_TFLOPS["bf16"] + 0.5 / PEAK_TFLOPS["fp8"])
+            extra[name + "_wan"] = {"ms": ms, "tflops": F / ms / 1e9, "frac_of_peak": F / ms / 1e9 / peak, "peak": peak,
+                                    "includes": "quantization + attention"}
+            del wsr
         del q4, k4, v4, ws, o_sage
         q2, k2, v2 = generate("dense_gqa_b2_h24kv8_s8192", device=dev)
         ms = timed_calls(lambda: dit.attn_dense_bf16(q2, k2, v2), 5, torch)
