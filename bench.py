@@ -257,7 +257,8 @@ def main():
         # SAGE FP8 (1,4,1) with Skip-Softmax on the same spatially peaked inputs
         # (quantization included); votes are 32 rows x one 64-key KV tile.
         sweep = {}
-        sage_votes = B * H * -(-S // vote_m) * -(-S // dit.kv_tile())
+        sv_m, sv_n = dit.sage_skip_tile()
+        sage_votes = B * H * -(-S // sv_m) * -(-S // sv_n)
         for f in (0.0, 1.0, 10.0, 100.0):
             cnt = {}
 

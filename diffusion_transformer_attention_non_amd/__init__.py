@@ -31,7 +31,7 @@ import torch
 __all__ = [
     "AttnError", "SageRecipe", "SkipGate", "attn_dense_bf16", "sage_quantize",
     "attn_sage", "attn_skip_softmax", "attn_sage_skip_softmax", "attention", "tile_config",
-    "kv_tile", "library_path",
+    "kv_tile", "sage_skip_tile", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,7 +95,7 @@ def _lib():
             "attn_skip_softmax": [P, P, P, P, I, SP, F, F, P, P, P, P],
             "attn_sage_skip_softmax": [P, P, P, P, I, SP, RP, F, F, P, P, P, ctypes.c_size_t, P],
             "attn_skip_gate": [F, F, ctypes.POINTER(I)],
-            "attn_tile_config": [ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)],
+            "attn_tile_config": [ctypes.POINTER(I)] * 4,
             "attn_version": [],
         }
         for name, args in sig.items():
@@ -118,18 +118,27 @@ def _check(rc: int):
     raise AttnError(f"ATTN_ERR_{name}: {msg}")
 
 
+def _tiles():
+    v = [ctypes.c_int() for _ in range(4)]
+    _check(_lib().attn_tile_config(*(ctypes.byref(x) for x in v)))
+    return [x.value for x in v]
+
+
 def tile_config():
-    """(block_m, block_n): query rows and keys per Skip-Softmax vote."""
-    bm, bn, kv = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(_lib().attn_tile_config(ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(kv)))
-    return bm.value, bn.value
+    """(block_m, block_n): query rows and keys per BF16 Skip-Softmax vote."""
+    bm, bn, _, _ = _tiles()
+    return bm, bn
 
 
 def kv_tile():
     """Keys per KV tile of the online softmax (SAGE's P rounding follows it)."""
-    bm, bn, kv = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(_lib().attn_tile_config(ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(kv)))
-    return kv.value
+    return _tiles()[2]
+
+
+def sage_skip_tile():
+    """(rows, keys) per vote of SAGE + Skip-Softmax: one KV tile of keys."""
+    _, _, kv, sbm = _tiles()
+    return sbm, kv
 
 
 def _stream(t: torch.Tensor):
@@ -367,8 +376,7 @@ def attn_sage_skip_softmax(q, k, v, recipe: SageRecipe, threshold_factor, out=No
     """SAGE attention with the Skip-Softmax tile test (threshold_factor / S_kv)
     on its dequantized logits, in one kernel.
 
-    The vote tile is block_m query rows x one KV tile (``tile_config()[0]`` x
-    ``kv_tile()``).  Returns out, or (out, extras) as attn_skip_softmax.
+    The vote tile is ``sage_skip_tile()``: 32 query rows x one 64-key KV tile.  Returns out, or (out, extras) as attn_skip_softmax.
     """
     _check_tensors(q, k, v)
     out, odt = _out(q, out, out_dtype)
@@ -376,8 +384,7 @@ def attn_sage_skip_softmax(q, k, v, recipe: SageRecipe, threshold_factor, out=No
     if workspace is None:
         workspace = torch.empty(max(1, lay.total_bytes), dtype=torch.uint8, device=q.device)
     shape = _shape(q, k, v, out)
-    bm, _ = tile_config()
-    kv = kv_tile()
+    bm, kv = sage_skip_tile()
     bitmap = cnt = None
     if return_bitmap:
         B, Sq, Hq, _ = q.shape

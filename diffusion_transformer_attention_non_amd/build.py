@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libditattn.so")
-SOURCES = ["abi.hip", "fmha_bf16.hip", "fmha_skip.hip", "fmha_sage.hip", "sage_quant.hip"]
+SOURCES = ["abi.hip", "fmha_bf16.hip", "fmha_sage.hip", "sage_quant.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

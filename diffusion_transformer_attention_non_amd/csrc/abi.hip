@@ -380,11 +380,12 @@ int attn_version(void) { return 100; }
 
 const char* attn_last_error(void) { return g_err; }
 
-int attn_tile_config(int* block_m, int* block_n, int* kv_tile) {
-  if (!block_m || !block_n || !kv_tile) return fail(ATTN_ERR_INVALID_ARG, "NULL output pointer");
-  *block_m = kWaveRows;
+int attn_tile_config(int* block_m, int* block_n, int* kv_tile, int* sage_block_m) {
+  if (!block_m || !block_n || !kv_tile || !sage_block_m) return fail(ATTN_ERR_INVALID_ARG, "NULL output pointer");
+  *block_m = kSkipBlockM;
   *block_n = kSkipBlockN;
   *kv_tile = kBlockN;
+  *sage_block_m = kWaveRows;
   return ok();
 }
 
@@ -438,7 +439,7 @@ int attn_skip_softmax(const void* q, const void* k, const void* v, void* o, attn
   if (threshold_factor == 0.0f) {
     // lambda = 0: nothing can be skipped; run the dense kernel itself.
     if (skip_bitmap) {
-      const int64_t nqb = (shape->S_q + kWaveRows - 1) / kWaveRows;
+      const int64_t nqb = (shape->S_q + kSkipBlockM - 1) / kSkipBlockM;
       const int64_t nkt = (shape->S_kv + kSkipBlockN - 1) / kSkipBlockN;
       const size_t n = (size_t)(shape->B * shape->Hq * nqb * nkt);
       if ((rc = launched(launch_fill_u8(skip_bitmap, n, 0, st), "bitmap clear"))) return rc;

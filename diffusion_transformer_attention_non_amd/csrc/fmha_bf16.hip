@@ -1,9 +1,11 @@
-// Dense BF16 attention for gfx950.
+// Dense and Skip-Softmax BF16 attention for gfx950.
 //
 // Fused multi-head attention O = softmax(sm_scale * Q K^T) V, full context,
 // non-causal ("TRTLLM Attention", section "Dense mode"; "Diffusion Attention
-// Backends", backend table: BF16, native GQA, head_dim 128).  The
-// Skip-Softmax variant is a separate kernel (fmha_skip.hip).
+// Backends", backend table: BF16, native GQA, head_dim 128), and with kSkip
+// the Skip-Softmax tile test ("TRTLLM Attention", section "Skip-Softmax";
+// threshold factor / seqlen from the knob table of "SAGE + Skip-Softmax -
+// API Design & Test Plan", Part 1 section 4).
 //
 // Work decomposition
 //   workgroup = 4 wavefronts = 256 query rows of one (batch, query head);
@@ -27,6 +29,15 @@
 //   blocks below); the order inside a block is written out (MFMA, its share
 //   of VALU work, scheduling fence), with LDS fragments read ahead.
 //
+// Skip-Softmax (kSkip): the vote tile is the wavefront's 64 rows x one
+// 32-key half.  Once a half's row maxima are known (the check after its Q
+// block) the wavefront drops it when every valid row i has
+// exp(M_it - m_i) < lambda, M_it the row's maximum over the half and m_i its
+// exact running maximum over the kept halves; lambda = factor / S_kv.  The
+// first half is kept.  A dropped half skips its BMM2 and row-sum MFMAs (the
+// Q block that carries them runs its VALU work alone) and changes no
+// softmax state; its speculative exponentials are simply unused.
+//
 // Online softmax with a lazy reference maximum: exponentials are taken
 // relative to a per-row reference m_ref (log2 units) that is raised only when
 // a tile's maximum exceeds it by more than 8, so P <= 2^8 and the O rescale
@@ -41,7 +52,7 @@
 namespace ditattn {
 namespace {
 
-constexpr int kDenseWaveRows = 64;   // query rows per wavefront
+constexpr int kDenseWaveRows = kSkipBlockM;   // query rows per wavefront (the skip vote's rows)
 constexpr int kDenseWaves = kBlockM / kDenseWaveRows;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -90,6 +101,7 @@ __device__ __forceinline__ int key_of_mfma_row(int i) {
 //      physical 16-byte chunk = logical chunk ^ (r & 15);
 //   V: row = key, physical 64-byte segment = logical segment ^ (key & 3).
 
+template <bool kSkip>
 __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
@@ -280,6 +292,14 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       fence();
     }
   };
+  // The VALU work of a Q block without its MFMAs (the half before was skipped).
+  auto valu_block = [&](auto&& valu) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      valu(t);
+      fence();
+    }
+  };
   // Exponential pipeline, pair k (0..15) of a half: qb = k / 8, 16-key step
   // s2 = (k / 4) % 2, register pair k % 4 of that step.
   float ex[3][2];       // pairs in flight, slot k % 3
@@ -387,14 +407,42 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   float mx0[2], mx1[2];
   f32x16 sb[2][2];       // dense: S^T of two halves in flight, [buffer][qb]
   bf16x8 pb[2][2][2];    // dense: P^T of two halves in flight, [buffer][16-key step][qb]
-  auto q_check = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2]) __attribute__((always_inline)) {
+  // Skip-Softmax state: exact running maxima over kept halves, the
+  // wavefront's skipped-half count and its bitmap row.
+  float mrun[2] = {kNegInf, kNegInf};
+  unsigned skipped = 0;
+  const int nvote = (Skv + kSkipBlockN - 1) / kSkipBlockN;
+  const bool qv0 = q0 + l32 < Sq, qv1 = q0 + 32 + l32 < Sq;
+  uint8_t* bitmap_row = nullptr;
+  if (kSkip && p.bitmap != nullptr && q0 < Sq)
+    bitmap_row = p.bitmap + ((int64_t)(b * p.Hq + h) * ((Sq + kSkipBlockM - 1) / kSkipBlockM) + q0 / kSkipBlockM) * nvote;
+  // After the Q block of half u: vote (kSkip), then move the reference if a
+  // kept half's maximum passed the slack.  Returns whether half u is kept.
+  auto q_check = [&](const f32x16 (&sv)[2], bf16x8 (&pout)[2][2], int u) __attribute__((always_inline)) -> bool {
     float mx[2];
     finish_max(mx);
+    if constexpr (kSkip) {
+      bool keep = false;   // halves past S_kv hold no keys: nothing to vote on or to add
+      if (u < nvote) {
+        keep = u == 0 || __any((qv0 && !(mx[0] - mrun[0] < p.log2_lambda)) ||
+                               (qv1 && !(mx[1] - mrun[1] < p.log2_lambda)));
+        if (bitmap_row != nullptr && lane == 0) bitmap_row[u] = keep ? 0 : 1;
+        if (!keep) ++skipped;
+      }
+      if (!keep) {
+        asm volatile("");
+        return false;
+      }
+      mrun[0] = fmaxf(mrun[0], mx[0]);
+      mrun[1] = fmaxf(mrun[1], mx[1]);
+    }
     if (needs_rescale(mx)) {
       rescale(mx);
       redo_q_pairs(sv, pout);
     }
+    return true;
   };
+  bool keep_b[2] = {true, true};   // kept flags of the halves in buffers 0 / 1
   if constexpr (true) {
     // S of half 0 (tile 0), then its Q-block VALU work with no BMM2 to pair with.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));
@@ -403,7 +451,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     mask_half(sb[0], 0);
 #pragma unroll
     for (int t = 0; t < 16; ++t) q_valu(sb[0], pb[0], t);
-    q_check(sb[0], pb[0]);
+    keep_b[0] = q_check(sb[0], pb[0], 0);
   }
 
   // ---- One KV tile (halves u0 = 2j, u1 = 2j+1): stage S = j % 4 holds tile j.
@@ -432,15 +480,23 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
         if ((t & 3) == 2) buffer_load_lds16(krsrc, kd + 4096 * (t >> 2), koff[t >> 2] + tk);
       });
       mask_half(sb[1], key0 + 32);
-      bmm2_block(vs, 0, pb[0], [&](int t) __attribute__((always_inline)) {
+      auto qv_odd = [&](int t) __attribute__((always_inline)) {
         q_valu(sb[1], pb[1], t);
         if ((t & 3) == 2) buffer_load_lds16(vrsrc, vd + 4096 * (t >> 2), voff[t >> 2] + tv);
-      });
-      q_check(sb[1], pb[1]);
+      };
+      if (!kSkip || keep_b[0])
+        bmm2_block(vs, 0, pb[0], qv_odd);
+      else
+        valu_block(qv_odd);
+      keep_b[1] = q_check(sb[1], pb[1], 2 * j + 1);
       bmm1_block(kst(IC<(S + 1) & 3>{}), 0, sb[0], [&](int t) __attribute__((always_inline)) { p_valu(sb[1], pb[1], t); });
       mask_half(sb[0], key0 + kBlockN);
-      bmm2_block(vs, 1, pb[1], [&](int t) __attribute__((always_inline)) { q_valu(sb[0], pb[0], t); });
-      q_check(sb[0], pb[0]);
+      auto qv_even = [&](int t) __attribute__((always_inline)) { q_valu(sb[0], pb[0], t); };
+      if (!kSkip || keep_b[1])
+        bmm2_block(vs, 1, pb[1], qv_even);
+      else
+        valu_block(qv_even);
+      keep_b[0] = q_check(sb[0], pb[0], 2 * j + 2);
     }
   };
 
@@ -455,6 +511,8 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     if (j + 4 >= nkt) break;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (kSkip && p.counter != nullptr && lane == 0 && q0 < Sq && skipped)
+    atomicAdd(p.counter, (unsigned long long)skipped);
 
   // ---- Epilogue: O = O^T / l, lane writes 4 consecutive d per register group.
 #pragma unroll
@@ -502,7 +560,15 @@ hipError_t launch_fmha_bf16(const FmhaBf16Args& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
   const int64_t nwg = nqt * a.Hq * a.B;
   if (nwg <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fmha_bf16_kernel, dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL(fmha_bf16_kernel<false>, dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fmha_bf16_skip(const FmhaBf16Args& a, hipStream_t stream) {
+  const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
+  const int64_t nwg = nqt * a.Hq * a.B;
+  if (nwg <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fmha_bf16_kernel<true>, dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

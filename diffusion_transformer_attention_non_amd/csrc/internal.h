@@ -8,12 +8,13 @@ namespace ditattn {
 
 // Tile geometry shared by the attention kernels and the host layer.
 constexpr int kHeadDim = 128;
-constexpr int kWaveRows = 32;    // query rows per wavefront in the SAGE and Skip-Softmax kernels
-                                  // (the Skip-Softmax decision unit)
+constexpr int kWaveRows = 32;    // query rows per wavefront in the low-precision (SAGE) kernel,
+                                  // its Skip-Softmax vote rows
 constexpr int kWavesPerWG = 8;   // two wavefronts per SIMD
-constexpr int kBlockM = kWaveRows * kWavesPerWG;  // query rows per workgroup
+constexpr int kBlockM = kWaveRows * kWavesPerWG;  // query rows per workgroup (every kernel)
 constexpr int kBlockN = 64;       // keys per KV tile (LDS stage)
-constexpr int kSkipBlockN = 32;   // keys per Skip-Softmax vote (half a KV tile)
+constexpr int kSkipBlockM = 64;   // BF16 kernels: query rows per wavefront = rows per Skip-Softmax vote
+constexpr int kSkipBlockN = 32;   // keys per BF16 Skip-Softmax vote (half a KV tile)
 constexpr int kMeanChunk = 256;   // tokens per partial sum of the K mean
 
 struct FmhaBf16Args {

@@ -182,14 +182,15 @@ int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o
  * knob table: threshold = factor / seqlen).
  *   As attn_sage, plus the tile test of attn_skip_softmax applied to the
  *   dequantized logits L of attn_sage (log2 units): queries in blocks of
- *   block_m rows, keys in the KV tiles of kv_tile keys (attn_tile_config: 32
- *   rows x 64 keys); tile t > 0 is skipped when every valid row i of the
+ *   sage_block_m rows, keys in the KV tiles of kv_tile keys
+ *   (attn_tile_config: 32 rows x 64 keys); tile t > 0 is skipped when every
+ *   valid row i of the
  *   block has 2^(M_it - m_i) < lambda = threshold_factor / S_kv, M_it the
  *   row's largest L in the tile and m_i its running maximum of L over the
  *   kept tiles.  A skipped tile changes nothing (not m_i, not the reference
  *   M, not the row sum).  threshold_factor = 0 runs exactly attn_sage
  *   (bit-identical).  skip_bitmap (nullable, device): [B, Hq,
- *   ceil(S_q/block_m), ceil(S_kv/kv_tile)] uint8, 1 = skipped; skipped_tiles
+ *   ceil(S_q/sage_block_m), ceil(S_kv/kv_tile)] uint8, 1 = skipped; skipped_tiles
  *   (nullable, device, 8-byte aligned): number of skipped (query block, KV
  *   tile) pairs.  ws as attn_sage.  Errors: as attn_sage, plus BAD_THRESHOLD
  *   (factor not finite or < 0). */
@@ -203,7 +204,7 @@ int attn_sage_skip_softmax(const void* q, const void* k, const void* v, void* o,
 /* Skip-Softmax attention on BF16 ([TA] "Skip-Softmax"; [SSD] knob table:
  * skip_softmax_threshold_scale_factor, threshold = factor / seqlen).
  *   lambda = threshold_factor / S_kv.  Queries are tiled in blocks of
- *   block_m rows and keys in tiles of block_n keys (attn_tile_config: 32
+ *   block_m rows and keys in tiles of block_n keys (attn_tile_config: 64
  *   rows x 32 keys).  For
  *   each query block, KV tiles are visited in ascending order; tile t > 0 is
  *   skipped when, for every valid row i of the block,
@@ -229,11 +230,12 @@ int attn_skip_softmax(const void* q, const void* k, const void* v, void* o,
 int attn_skip_gate(float t, float disabled_until_timestep, int* enabled);
 
 /* Tile sizes of the attention kernels: block_m query rows and block_n keys
- * per Skip-Softmax vote of attn_skip_softmax (the skip bitmap's tile), and
+ * per Skip-Softmax vote of attn_skip_softmax (the skip bitmap's tile),
  * kv_tile keys per KV tile of the online softmax (the tile order SAGE's P
- * rounding follows; attn_sage_skip_softmax votes on block_m rows x kv_tile
- * keys).  Host-only. */
-int attn_tile_config(int* block_m, int* block_n, int* kv_tile);
+ * rounding follows), and sage_block_m query rows per vote of
+ * attn_sage_skip_softmax (which votes on sage_block_m rows x kv_tile keys).
+ * Host-only. */
+int attn_tile_config(int* block_m, int* block_n, int* kv_tile, int* sage_block_m);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* attn_last_error(void);

@@ -40,7 +40,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_host_queries():
-    assert dit.tile_config() == (32, 32)
+    assert dit.tile_config() == (64, 32)
+    assert dit.sage_skip_tile() == (32, 64)
     assert dit.kv_tile() == 64
     assert dit._lib().attn_version() >= 100
 

@@ -71,7 +71,7 @@ def test_skip_softmax_with_recipe_matches_oracle(rec):
                                        return_bitmap=True, return_count=True)
     torch.cuda.synchronize()
     quant = sage_quantize(q, k, v, *rec)
-    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 10.0, dit.tile_config()[0], dit.kv_tile())
+    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 10.0, *dit.sage_skip_tile())
     got = ex["bitmap"].cpu().numpy().astype(bool)
     lam = 10.0 / q.shape[1]
     with np.errstate(divide="ignore", invalid="ignore"):

@@ -59,7 +59,7 @@ def test_skip_set_and_output_match_oracle(grid, Hq, Hkv, dt, qb, kb, factor):
     o, ex = dit.attn_sage_skip_softmax(q.cuda(), k.cuda(), v.cuda(), rec, factor, out_dtype=torch.float32,
                                        return_bitmap=True, return_count=True)
     torch.cuda.synchronize()
-    bm, _ = dit.tile_config()
+    bm, _ = dit.sage_skip_tile()
     quant = sage_quantize(q, k, v, dt, qb, kb)
     ref, skipped, ratio, rows = sage_skip_attention(quant, SC, factor, bm, dit.kv_tile())
     got = ex["bitmap"].cpu().numpy().astype(bool)
@@ -82,7 +82,7 @@ def test_gaussian_inputs_rarely_skip():
                                        return_bitmap=True)
     torch.cuda.synchronize()
     quant = sage_quantize(q, k, v, "fp8", 1, 4)
-    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 1.0, dit.tile_config()[0], dit.kv_tile())
+    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 1.0, *dit.sage_skip_tile())
     flips = _compare(ex["bitmap"].cpu().numpy().astype(bool), skipped, ratio, 1.0 / 1000)
     r = rel_l2(to_np(o), ref)
     assert r <= 3e-2 and (flips or r <= 5e-3), r
@@ -102,7 +102,7 @@ def test_wan_shape_sampled_tiles():
     qd, kd, vd = generate("skip_wan_b1_h40_s75600", device="cuda")
     q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
     rec = dit.SageRecipe("fp8", "fp8", 1, 4, 1)
-    bm, _ = dit.tile_config()
+    bm, _ = dit.sage_skip_tile()
     S = q.shape[1]
     nqb = -(-S // bm)
     heads = [0, 39]
