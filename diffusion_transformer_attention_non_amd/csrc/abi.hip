@@ -276,7 +276,6 @@ SageQuantArgs quant_args(const void* q, const void* k, const void* v, const attn
   a.Skv = (int)s->S_kv;
   a.Hq = (int)s->Hq;
   a.Hkv = (int)s->Hkv;
-  a.qk_int8 = r->qk_dtype == ATTN_DTYPE_INT8;
   a.qk_fmt = qk_fmt(r);
   a.smooth = a.qk_fmt == kQkInt8 || a.qk_fmt == kQkFp8;
   a.v_tensor = r->v_block == 0;
@@ -343,7 +342,6 @@ int run_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_
   a.n_kblk = L.n_kblk;
   a.q_block = recipe->q_block;
   a.k_block = recipe->k_block;
-  a.qk_int8 = qa.qk_int8;
   a.qk_fmt = qa.qk_fmt;
   a.q_mx = qa.q_mx;
   a.k_mx = qa.k_mx;

@@ -46,7 +46,6 @@ struct SageQuantArgs {
   const void* v;
   int64_t qs[3], ks[3], vs[3];
   int B, Sq, Skv, Hq, Hkv;
-  int qk_int8;          // 1 = int8 codes, 0 = E4M3 codes (token-block scales)
   int qk_fmt;           // kQk*
   int smooth;           // 1 = K-smoothing (SageAttention recipes)
   int v_tensor;         // 1 = one tensor-wide V scale, 0 = one per (b, kv head, channel)
@@ -85,7 +84,6 @@ struct FmhaSageArgs {
   int B, Sq, Skv, Hq, Hkv;
   int64_t s_pad, n_qblk, n_kblk;
   int q_block, k_block;
-  int qk_int8;
   float sm_scale;
   int o_fp32;
   int skip;                         // 1 = Skip-Softmax tile test on (32 rows x one KV tile)
