@@ -28,12 +28,13 @@
 //   softmax with a power-of-two reference: m' = max(m, ceil(tile max of L)),
 //         P = E4M3(2^(L - m' + 8)), l += sum P (the values BMM2 multiplies);
 //   BMM2  O^T += Vc^T P^T on E4M3 codes (v_mfma_scale_f32_32x32x64_f8f6f4,
-//         V^T codes d-major as the quantizer writes them), plus one all-ones
-//         MFMA for the row sums.
-//   O and l stay relative to an older integer reference mo; both MFMAs take
-//   P times 2^(m - mo) through their E8M0 B scale, so moving m never touches
-//   O.  Only if m - mo would leave the safe range is O rescaled, exactly.
-//   Epilogue O = acc * sv_d / l (bmm2 scale).
+//         V^T codes d-major as the quantizer writes them), plus one 16x16x128
+//         selector MFMA for the row sums.
+//   O stays relative to an older integer reference mo: BMM2 takes P times
+//   2^(m - mo) through its E8M0 B scale, so moving m never touches O.  Only
+//   if m - mo would leave the safe range is O rescaled, exactly.  The four
+//   row-sum registers follow m instead (an exact power-of-two rescale when
+//   m moves).  Epilogue O = acc * sv_d * 2^(mo - m) / l (bmm2 scale).
 //
 // Skip-Softmax (kSkip; both options in one kernel, "TRTLLM Attention",
 // section "Skip-Softmax", and "VisualGen Quantized Attention", section
@@ -264,14 +265,22 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  // Row sums: an all-ones A operand makes every row of the result the column
-  // (query) sum of P; register 0 of lane l holds query l % 32.
-  f32x16 lrow;
+  // Row sums: v_mfma_f32_16x16x128_f8f6f4 (unscaled) with B = the BMM2
+  // operand P^T (lane l: query l % 32, keys 32 (l / 32) + 0..31 = column
+  // l % 16, k group l / 16) and a 0/1 selector A (E4M3 1.0 = 0x38) whose row
+  // 0 takes k groups 0 and 2 (queries 0..15) and row 1 groups 1 and 3
+  // (queries 16..31).  Register r of lane n < 16 then holds the row sum of
+  // query 16 r + n, relative to the current reference m (P = 2^(L - m + 8)),
+  // so lrow is rescaled whenever m moves.
+  f32x4 lrow = {0.0f, 0.0f, 0.0f, 0.0f};
+  i32x8 rsel;
+  {
+    const int mrow = lane & 15, grp = lane >> 4;
+    const int one = (mrow < 2 && mrow == (grp & 1)) ? 0x38383838 : 0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) lrow[r] = 0.0f;
-  i32x8 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                 0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
-  asm volatile("" : "+v"(ones8));   // kept in registers, not rebuilt before every use
+    for (int i = 0; i < 8; ++i) rsel[i] = one;
+  }
+  asm volatile("" : "+v"(rsel));   // kept in registers, not rebuilt before every use
 
   float m = kNegInf, mo = kNegInf;   // reference and O reference (integers, log2 units)
   int bsc = 127;                      // E8M0 scale 2^(m - mo)
@@ -393,12 +402,14 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     const float mnew = fmaxf(m, __builtin_ceilf(lmax));
     if (__any(mnew > m)) {
       if (m == kNegInf) mo = mnew;   // the first tile fixes the O reference
+      // lrow follows m: scale it by 2^(m_old - m_new), exact (integers; 0 on the first tile)
+      const float fl = exp2_fast(m - mnew);
+      lrow[0] *= fl;
+      lrow[1] *= __shfl(fl, (lane & 15) + 16, 64);
       m = mnew;
       if (__any(m - mo > kMaxRefGap)) {
         const float f = exp2_fast(mo - m);   // exact: the difference is an integer
         mo = m;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lrow[r] *= f;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -428,7 +439,7 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
       const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, o[db], 0, 0, 0, 127, 0, bsc);
     }
-    lrow = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, pf, lrow, 0, 0, 0, 127, 0, bsc);
+    lrow = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rsel, pf, lrow, 0, 0, 0, 127, 0, 127);
   };
 
   // ---- Tiles: stage t % 4 holds tile t.  Step t: BMM1 of tile t+1 goes out
@@ -471,7 +482,9 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
 
   // ---- Epilogue: O = O^T * sv_d / l.
   const float* svp = p.v_scale + ((int64_t)b * p.Hkv + g) * kHeadDim;
-  const float inv = 1.0f / lrow[0];
+  // O is relative to mo, l to m: O / l carries the exact factor 2^(mo - m).
+  const float l_lo = __shfl(lrow[0], l32 & 15, 64), l_hi = __shfl(lrow[1], l32 & 15, 64);
+  const float inv = exp2_fast(mo - m) / (l32 < 16 ? l_lo : l_hi);
   const int row = q0 + l32;
   if (row < Sq) {
     const int64_t obase = b * p.os[0] + (int64_t)row * p.os[1] + h * p.os[2];
