@@ -45,6 +45,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fmha_bf16_dense_wan_traffic.json"
 KERNEL_SRC = os.path.join(ROOT, "diffusion_transformer_attention_non_amd", "csrc", "fmha_bf16.hip")
 
 
+PROFILE_CALLS = ("dense_bf16", "skip_bf16_factor1", "sage_fp8_141", "sage_int8_1161_s32768", "mxfp8_001",
+                 "qk16pv8_000")
+
+
 def eff_flops(B, S, H, D=128, Skv=None):
     return 4.0 * B * H * S * (S if Skv is None else Skv) * D
 
@@ -57,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the factor sweep")
+    ap.add_argument("--profile-call", choices=PROFILE_CALLS, default=None,
+                    help="run only this attention call (warmup + steps launches) for counter collection")
     return ap.parse_args()
 
 
@@ -139,6 +145,36 @@ def cpu_baseline(budget_s, S, H, step_flops):
     }
 
 
+def profile_call(args, dit, generate, torch, dev):
+    """One attention call kind only, for rocprofv3 counter passes: the same
+    inputs and recipes as the bench step (the int8 SAGE one at S=32,768)."""
+    name = args.profile_call
+    if name in ("dense_bf16", "skip_bf16_factor1"):
+        q, k, v = generate("skip_wan_b1_h40_s75600", device=dev)
+    elif name == "sage_int8_1161_s32768":
+        q, k, v = generate("sage_int8_b1_h40_s32768", device=dev)
+    else:
+        q, k, v = generate("sage_fp8_wan_b1_h40_s75600", device=dev)
+    o = torch.empty_like(q)
+    recipes = {"sage_fp8_141": ("fp8", 1, 4, 1), "sage_int8_1161_s32768": ("int8", 1, 16, 1),
+               "mxfp8_001": ("mxfp8", 0, 0, 1), "qk16pv8_000": ("bf16", 0, 0, 0)}
+    if name == "dense_bf16":
+        fn = lambda: dit.attn_dense_bf16(q, k, v, out=o)
+    elif name == "skip_bf16_factor1":
+        fn = lambda: dit.attn_skip_softmax(q, k, v, SKIP_FACTOR, out=o)
+    else:
+        rt = recipes[name]
+        rec = dit.SageRecipe(rt[0], "fp8", *rt[1:])
+        ws = dit.sage_workspace(q, k, v, rec)
+        fn = lambda: dit.attn_sage(q, k, v, rec, out=o, workspace=ws)
+    for _ in range(args.warmup):
+        fn()
+    ms = timed_calls(fn, args.steps, torch)
+    B, S, H = q.shape[0], q.shape[1], q.shape[2]
+    print(json.dumps({"profile_call": name, "launches": args.warmup + args.steps, "ms": ms,
+                      "effective_flops_per_call": eff_flops(B, S, H)}))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -156,6 +192,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.profile_call:
+        profile_call(args, dit, generate, torch, dev)
+        return
     B, S, H, D = WAN["B"], WAN["S"], WAN["H"], WAN["D"]
     print(f"[bench] generating Wan-shaped inputs B={B} S={S} H={H} D={D}", file=sys.stderr, flush=True)
     q5, k5, v5 = generate("skip_wan_b1_h40_s75600", device=dev)
