@@ -359,19 +359,38 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   };
   // Softmax of S(tile) (keys key0..key0+63, scales and V^T in stage sm), then BMM2.
   auto softmax_bmm2 = [&](const uint8_t* sm, f32x16 (&s)[2], int key0) __attribute__((always_inline)) {
-    // Dequantization (K scale per key; SageAttention only), tail mask, row maximum.
+    // The exponent argument y = L - m + 8 with L = acc * sk * qsc.  With a
+    // block of four or more keys per K scale (kFold) the per-key factor
+    // sk * qsc is formed once per four keys and y comes from one fma with the
+    // reference as it stands; if the tile then moves m, y is shifted by the
+    // (integer) change.  Otherwise the K scale (SageAttention) is applied
+    // first and y = fma(acc', qsc, 8 - m) once m is known.  (With the skip
+    // vote the folded form runs out of registers, so it keeps the other.)
+    constexpr bool kFold = kTokScales && kBlock4 && !kSkip;
+    const float mt = m == kNegInf ? 0.0f : m;   // reference folded into y (kFold)
+    if constexpr (kFold) {
+      const float nb0 = 8.0f - mt;
 #pragma unroll
-    for (int gq = 0; gq < 8 && kTokScales; ++gq) {
-      const int kb = gq >> 2, r0 = 4 * (gq & 3);
-      f32x4 sk;
-      if constexpr (kBlock4) {
-        const float s1 = *reinterpret_cast<const float*>(sm + sa + 4 * (16 * kb + r0));
-        sk = f32x4{s1, s1, s1, s1};
-      } else {
-        sk = *reinterpret_cast<const f32x4*>(sm + sa + 4 * (16 * kb + r0));
+      for (int gq = 0; gq < 8; ++gq) {
+        const int kb = gq >> 2, r0 = 4 * (gq & 3);
+        const float f = *reinterpret_cast<const float*>(sm + sa + 4 * (16 * kb + r0)) * qsc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[kb][r0 + j] = __builtin_fmaf(s[kb][r0 + j], f, nb0);
       }
+    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[kb][r0 + j] *= sk[j];
+      for (int gq = 0; gq < 8 && kTokScales; ++gq) {
+        const int kb = gq >> 2, r0 = 4 * (gq & 3);
+        f32x4 sk;
+        if constexpr (kBlock4) {
+          const float s1 = *reinterpret_cast<const float*>(sm + sa + 4 * (16 * kb + r0));
+          sk = f32x4{s1, s1, s1, s1};
+        } else {
+          sk = *reinterpret_cast<const f32x4*>(sm + sa + 4 * (16 * kb + r0));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[kb][r0 + j] *= sk[j];
+      }
     }
     if (key0 + kBlockN > Skv) {   // the tile that holds S_kv: a real branch, not selects on every tile
       asm volatile("");
@@ -386,7 +405,8 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
-    const float lmax = max_halves(mx) * qsc;   // row maximum of L over the tile
+    // row maximum of L over the tile
+    const float lmax = kFold ? max_halves(mx) - (8.0f - mt) : max_halves(mx) * qsc;
     if constexpr (kSkip) {
       const int t = key0 / kBlockN;
       const bool keep = t == 0 || __any(qvalid && !(lmax - mrun < p.log2_lambda));
@@ -416,8 +436,15 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
           for (int r = 0; r < 16; ++r) o[db][r] *= f;
       }
       bsc = 127 + (int)(m - mo);
+      if constexpr (kFold) {   // y was taken against mt: shift it to the new reference (exact)
+        const float d = mt - m;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] += d;
+      }
     }
-    // P = E4M3(2^(L - m + 8)): byte 16 kb + r of this lane half is key 32 hh + 16 kb + r.
+    // P = E4M3(2^y): byte 16 kb + r of this lane half is key 32 hh + 16 kb + r.
     const float nb = 8.0f - m;
     i32x8 pf;
 #pragma unroll
@@ -425,7 +452,7 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
       const int kb = w >> 2, r0 = 4 * (w & 3);
       float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[j] = exp2_fast(__builtin_fmaf(s[kb][r0 + j], qsc, nb));
+      for (int j = 0; j < 4; ++j) x[j] = exp2_fast(kFold ? s[kb][r0 + j] : __builtin_fmaf(s[kb][r0 + j], qsc, nb));
       // The low half is written over x[0]'s own register (x[0] is dead after
       // this), so no copy of an "old" value is needed.
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __builtin_bit_cast(int, x[0]), false);
