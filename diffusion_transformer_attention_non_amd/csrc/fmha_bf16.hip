@@ -424,8 +424,11 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     if constexpr (kSkip) {
       bool keep = false;   // halves past S_kv hold no keys: nothing to vote on or to add
       if (u < nvote) {
-        keep = u == 0 || __any((qv0 && !(mx[0] - mrun[0] < p.log2_lambda)) ||
-                               (qv1 && !(mx[1] - mrun[1] < p.log2_lambda)));
+        // Past the first half every valid row has a finite running maximum
+        // and a finite half maximum, so >= is the negation of <.  Bitwise
+        // operators keep the vote free of branches.
+        const bool hot = (qv0 & (mx[0] - mrun[0] >= p.log2_lambda)) | (qv1 & (mx[1] - mrun[1] >= p.log2_lambda));
+        keep = u == 0 || __any(hot);
         if (bitmap_row != nullptr && lane == 0) bitmap_row[u] = keep ? 0 : 1;
         if (!keep) ++skipped;
       }
@@ -433,8 +436,8 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
         asm volatile("");
         return false;
       }
-      mrun[0] = fmaxf(mrun[0], mx[0]);
-      mrun[1] = fmaxf(mrun[1], mx[1]);
+      mrun[0] = max_raw(mrun[0], mx[0]);
+      mrun[1] = max_raw(mrun[1], mx[1]);
     }
     if (needs_rescale(mx)) {
       rescale(mx);
