@@ -250,6 +250,12 @@ int check_sage(const void* q, const void* k, const void* v, const attn_shape* sh
   if ((rc = check_recipe(recipe))) return rc;
   sage_layout(shape, recipe, L);
   if (empty(shape) && shape->S_kv == 0) return ATTN_OK;
+  // The low-precision kernel addresses one head's codes (and, for BF16 Q/K,
+  // its K rows) through 32-bit buffer offsets, including tiles past the end.
+  if ((L->s_pad + 4 * kBlockN) * kHeadDim >= ((int64_t)1 << 32))
+    return fail(ATTN_ERR_INVALID_ARG, "codes of one head exceed 4 GiB (S too large)");
+  if (qk_fmt(recipe) == kQkBf16 && (shape->S_kv + 4 * kBlockN) * shape->k_stride[1] * 2 >= ((int64_t)1 << 32))
+    return fail(ATTN_ERR_INVALID_ARG, "K span of one head exceeds 4 GiB");
   if (!q || !k || !v) return fail(ATTN_ERR_INVALID_ARG, "q, k and v must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(ATTN_ERR_BAD_LAYOUT, "q, k, v must be 16-byte aligned");
   if (ws == nullptr) return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL");

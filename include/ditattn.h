@@ -34,6 +34,14 @@
  *     h reads KV head h / (Hq / Hkv) ("GQA native", [DAB] backend table).
  *   - Attention is full-context and non-causal; there is no mask argument
  *     ([TA] "Requirements": a packed or mask-free path).
+ *   - Size limits (INVALID_ARG beyond them, checked before any device call):
+ *     S_q, S_kv and B * Hq below 2^31 and fewer than 2^31 workgroups; the
+ *     kernels address one (batch, kv head)'s rows through 32-bit byte
+ *     offsets, so (S_kv + 256) * k_stride[1] * 2 and the same for v_stride
+ *     must stay below 4 GiB on the BF16 paths (with packed QKV of 40 heads,
+ *     S_kv up to about 139,000), and for the quantized paths the padded
+ *     sequence (S rounded up to 64, plus 256) times 128 bytes as well
+ *     (S up to about 33.5 million).
  *   - Calls that run on the same stream are ordered; concurrent calls on
  *     different streams that share an output buffer or workspace race.
  */

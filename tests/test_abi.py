@@ -212,3 +212,27 @@ def test_sage_skip_threshold_and_workspace_checked_before_device():
     assert call(float("inf")) == THRESHOLD
     assert call(1.0, wsb=10) == WS
     assert call(1.0, r=_recipe(2, 3, 16)) == RECIPE
+
+
+def test_size_limits_rejected_before_device():
+    lib = dit._lib()
+    big = 1 << 31
+    assert _dense(_shape(S=big)) == INVALID
+    assert b"too large" in lib.attn_last_error()
+    assert _dense(_shape(B=1 << 16, Hq=1 << 15, Hkv=1 << 15)) == INVALID
+    assert _dense(_shape(S=1 << 30, Hq=1 << 9, Hkv=1 << 9)) == INVALID   # 2^31 workgroups
+    assert b"one launch" in lib.attn_last_error()
+    # one head's K rows span (S_kv + 256) * k_stride[1] * 2 bytes through 32-bit offsets
+    s = _shape(S=1 << 24, Hq=1, Hkv=1)
+    assert _dense(s) == INVALID
+    assert b"4 GiB" in lib.attn_last_error()
+    s = _shape(S=(1 << 24) - 512, Hq=1, Hkv=1)
+    assert _dense(s) in (DEVICE, OK)               # inside the limit: only the device check remains
+    # the quantized path: codes of one head through 32-bit offsets
+    rec = _recipe(3, 1, 4)
+    ws = ctypes.c_void_p(0x100000)
+    s = _shape(S=1 << 25, Hq=1, Hkv=1)
+    rc = lib.attn_sage(FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(rec), ctypes.c_float(0.088),
+                       ws, ctypes.c_size_t(1 << 62), None)
+    assert rc == INVALID
+    assert b"4 GiB" in lib.attn_last_error()
