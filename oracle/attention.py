@@ -218,7 +218,7 @@ def _mx_quant_rows(x):
     return e4m3_encode(y.reshape(S, D)), exp.astype(np.int64)
 
 
-def sage_quantize(q, k, v, qk_dtype, q_block, k_block, v_block=1):
+def sage_quantize(q, k, v, qk_dtype, q_block, k_block, v_block=1, v_amax=None):
     """Quantization of Q, K and V for the low-precision attention recipes.
 
     The recipe is (qk_dtype, v_dtype = fp8, (q_block, k_block, v_block))
@@ -235,7 +235,9 @@ def sage_quantize(q, k, v, qk_dtype, q_block, k_block, v_block=1):
         smoothing (the pages tie smoothing to SageAttention only).
       * V: fp8 E4M3 with one scale per (batch, KV head, channel) for
         v_block = 1, or one tensor-wide scale for v_block = 0; scale =
-        binary32(max|v| / 448) (1 if all zero).
+        binary32(max|v| / 448) (1 if all zero).  ``v_amax`` supplies the
+        tensor-wide max|v| for v_block = 0 when ``v`` holds only some heads
+        of the tensor (it must be at least the slice's own maximum).
 
     Returns a dict: q_codes [B,Hq,S,D], k_codes [B,Hkv,S,D] (int8, uint8
     E4M3 bits, or float32 BF16 values), q_scale / k_scale (binary32 per token
@@ -291,7 +293,12 @@ def sage_quantize(q, k, v, qk_dtype, q_block, k_block, v_block=1):
                 out["k_codes"][b, g] = kf[b, :, g]
     vmax = np.float32(E4M3_MAX)
     if v_block == 0:
-        a = np.float32(np.abs(vf).max()) if vf.size else np.float32(0.0)
+        if v_amax is not None:   # the tensor-wide maximum, when v is a slice (some heads) of the tensor
+            a = np.float32(v_amax)
+            if vf.size and np.abs(vf).max() > a:
+                raise ValueError("v_amax is below the largest |v| of the slice")
+        else:
+            a = np.float32(np.abs(vf).max()) if vf.size else np.float32(0.0)
         out["v_scale"][...] = np.float32(1.0) if a == 0 else np.float32(a / vmax)
     else:
         a = np.abs(vf).max(axis=1)                                 # [B, Hkv, D]

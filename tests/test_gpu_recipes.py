@@ -82,19 +82,23 @@ def test_skip_softmax_with_recipe_matches_oracle(rec):
     assert r_ <= 3e-2 and (((got != skipped) & near).any() or r_ <= 5e-3), r_
 
 
-def test_mxfp8_wan_shape_sampled():
-    """B=1, H=40, S=75,600 Gaussian inputs with K bias and outlier channels, MXFP8 Q/K, per-channel V; sampled rows."""
-    announce("mxfp8 wan generate")
+@pytest.mark.parametrize("rec", [("mxfp8", 0, 0, 1), ("bf16", 0, 0, 0)])
+def test_wan_shape_sampled(rec):
+    """B=1, H=40, S=75,600 Gaussian inputs with K bias and outlier channels: MXFP8 Q/K with
+    per-channel V, and QK16PV8 (BF16 Q/K, tensor-wide V scale); sampled rows of two heads."""
+    dt, qb, kb, vb = rec
+    announce(f"{dt} ({qb},{kb},{vb}) wan generate")
     qd, kd, vd = generate("sage_fp8_wan_b1_h40_s75600", device="cuda")
-    r = dit.SageRecipe("mxfp8", "fp8", 0, 0, 1)
-    announce("mxfp8 wan attention")
+    r = dit.SageRecipe(dt, "fp8", qb, kb, vb)
+    announce(f"{dt} wan attention")
     o = dit.attn_sage(qd, kd, vd, r)
     torch.cuda.synchronize()
     q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
     rows = np.concatenate([np.arange(0, 32), np.arange(40000, 40032), np.arange(75568, 75600)])
+    v_amax = float(v.float().abs().max()) if vb == 0 else None   # tensor-wide V scale spans every head
     for h in (0, 39):
         sl = slice(h, h + 1)
-        quant = sage_quantize(q[:, :, sl], k[:, :, sl], v[:, :, sl], "mxfp8", 0, 0, 1)
+        quant = sage_quantize(q[:, :, sl], k[:, :, sl], v[:, :, sl], dt, qb, kb, vb, v_amax=v_amax)
         emu = sage_attention(quant, SC, dit.kv_tile(), rows=rows)
         rr = rel_l2(to_np(o[:, rows, sl]), emu)
         assert rr <= 3e-2, (h, rr)

@@ -11,6 +11,7 @@ import torch
 from oracle import E4M3_MAX, e4m3_decode, e4m3_encode, exact_attention, sage_attention, sage_quantize, \
     sage_skip_attention
 from oracle.attention import _mx_quant_rows
+from diffusion_transformer_attention_non_amd.synth import gaussian_qkv
 
 SC = 1 / math.sqrt(128)
 E4M3_VALUES = np.unique(np.abs(e4m3_decode(np.arange(256, dtype=np.uint8))))
@@ -166,3 +167,17 @@ def test_skip_on_mxfp8_reduces_to_sage_at_factor_zero():
     quant = sage_quantize(q, k, v, "mxfp8", 0, 0, 1)
     o, sk, _, rows = sage_skip_attention(quant, SC, 0.0, 32, 64)
     assert not sk.any() and np.array_equal(o, sage_attention(quant, SC, 64, rows=rows))
+
+
+def test_tensor_wide_v_scale_from_a_slice():
+    """v_amax: quantizing one head with the tensor-wide maximum gives that head's part of
+    the whole-tensor quantization ("Recipes": one V scale for the whole tensor)."""
+    q, k, v = gaussian_qkv(1, 40, 2, 2, seed=5)
+    full = sage_quantize(q, k, v, "bf16", 0, 0, 0)
+    amax = float(np.abs(v.float().numpy()).max())
+    for h in range(2):
+        part = sage_quantize(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], "bf16", 0, 0, 0, v_amax=amax)
+        assert np.array_equal(part["v_codes"][:, 0], full["v_codes"][:, h])
+        assert np.array_equal(part["v_scale"][:, 0], full["v_scale"][:, h])
+    with pytest.raises(ValueError):
+        sage_quantize(q, k, v, "bf16", 0, 0, 0, v_amax=amax / 2)
