@@ -143,3 +143,20 @@ def test_lse_factor_zero_and_kept_key_set(peaked):
         _, ref = exact_attention(q[:, :, h:h + 1], k[:, keys, h:h + 1], v[:, keys, h:h + 1], SC, rows=rows,
                                  return_lse=True)
         np.testing.assert_allclose(lse[0, h], ref[0, 0], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("delta,skipped", [(-0.01, True), (0.01, False)])
+def test_threshold_boundary_is_factor_over_seqlen_in_natural_log(delta, skipped):
+    """Tile 1's maximum sits ln(lambda) + delta below tile 0's, lambda = factor / S_kv = 4 / 64
+    ("threshold = factor / seqlen"; the tile is dropped when exp(M - m) < lambda).  A threshold
+    without the division by S_kv, or taken in log2 units, puts both cases on the same side."""
+    S, D, bn = 64, 128, 32
+    lam = 4.0 / S
+    q = np.zeros((1, S, 1, D))
+    k = np.zeros((1, S, 1, D))
+    q[0, :, 0, 0] = 1.0
+    k[0, bn:, 0, 0] = math.log(lam) + delta
+    v = np.random.default_rng(1).standard_normal((1, S, 1, D))
+    _, sk, _, _ = skip_attention(q, k, v, 1.0, 4.0, 64, bn)
+    assert not sk[..., 0].any()
+    assert bool(sk[0, 0, 0, 1]) == skipped
