@@ -98,3 +98,24 @@ def test_every_later_tile_skipped_when_maxima_fall():
     first["v_codes"] = quant["v_codes"][:, :, :bn]
     first["k_scale"] = quant["k_scale"][:, :, :bn]
     assert np.array_equal(o, sage_attention(first, 1.0, bn))
+
+
+@pytest.mark.parametrize("delta,skipped", [(-0.01, True), (0.01, False)])
+def test_threshold_boundary_in_log2_units(delta, skipped):
+    """QK16PV8 codes (exact BF16 values): tile 1's largest logit, in log2 units, sits
+    log2(lambda) + delta under tile 0's, lambda = factor / S_kv = 4 / 64; the tile is dropped
+    exactly when 2^(M - m) < lambda.  Comparing log2-unit logits with ln(lambda), or a
+    threshold without the division by S_kv, puts both cases on the same side."""
+    import torch
+    S, bn = 64, 32
+    lam = 4.0 / S
+    q = torch.zeros(1, S, 1, 128)
+    k = torch.zeros(1, S, 1, 128)
+    v = torch.randn(1, S, 1, 128, generator=torch.Generator().manual_seed(2))
+    q[0, :, 0, 0] = 1.0
+    k[0, bn:, 0, 0] = -1.0
+    sm = -(math.log2(lam) + delta) * math.log(2.0)   # L = sm * (-1) * log2(e) = log2(lam) + delta
+    quant = sage_quantize(q.bfloat16(), k.bfloat16(), v.bfloat16(), "bf16", 0, 0, 0)
+    _, sk, _, _ = sage_skip_attention(quant, sm, 4.0, 64, bn)
+    assert not sk[..., 0].any()
+    assert bool(sk[0, 0, 0, 1]) == skipped
