@@ -120,3 +120,25 @@ def test_wan_shape_sampled_tiles():
             r = rel_l2(to_np(o[:, rows, h:h + 1]), ref)
             assert r <= 3e-2, (factor, h, r)
         print(f"factor {factor}: skipped fraction {bitmap.mean():.4f}")
+
+
+@pytest.mark.parametrize("delta,skipped", [(-0.01, True), (0.01, False)])
+def test_threshold_boundary_qk16pv8(delta, skipped):
+    """QK16PV8 codes are the exact BF16 inputs: the second 64-key tile's logits sit
+    log2(lambda) + delta (log2 units) under the first tile's, lambda = factor / S_kv = 4 / 128;
+    the kernel drops the tile exactly when 2^(M - m) < lambda."""
+    S = 128
+    announce(f"sage skip threshold boundary delta={delta}")
+    q = torch.zeros(1, S, 1, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, S, 1, 128, dtype=torch.bfloat16)
+    q[0, :, 0, 0] = 1.0
+    k[0, 64:, 0, 0] = -1.0
+    v = torch.randn(1, S, 1, 128, generator=torch.Generator().manual_seed(4)).bfloat16()
+    sm = -(math.log2(4.0 / S) + delta) * math.log(2.0)
+    rec = dit.SageRecipe("bf16", "fp8", 0, 0, 0)
+    o, ex = dit.attn_sage_skip_softmax(q.cuda(), k.cuda(), v.cuda(), rec, 4.0, sm_scale=sm, return_bitmap=True,
+                                       return_count=True)
+    torch.cuda.synchronize()
+    bm = ex["bitmap"].cpu().numpy()
+    assert bm.shape[-1] == 2 and not bm[0, 0, :, 0].any()
+    assert np.all(bm[0, 0, :, 1] == int(skipped))

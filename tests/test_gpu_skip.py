@@ -125,3 +125,24 @@ def test_lse_over_kept_keys():
     if flips == 0:
         err = np.abs(to_np(ex["lse"]) - ref_lse).max()
         assert err <= 4e-3, err
+
+
+@pytest.mark.parametrize("delta,skipped", [(-0.01, True), (0.01, False)])
+def test_threshold_boundary(delta, skipped):
+    """The second 32-key half's logits sit ln(lambda) + delta under the first half's (0),
+    lambda = factor / S_kv = 4 / 64: the kernel drops the half exactly when exp(M - m) < lambda
+    (BF16 inputs are exact here; sm_scale carries the offset)."""
+    S = 64
+    announce(f"skip threshold boundary delta={delta}")
+    q = torch.zeros(1, S, 1, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, S, 1, 128, dtype=torch.bfloat16)
+    q[0, :, 0, 0] = 1.0
+    k[0, 32:, 0, 0] = -1.0
+    v = torch.randn(1, S, 1, 128, generator=torch.Generator().manual_seed(3)).bfloat16()
+    sm = -(math.log(4.0 / S) + delta)
+    o, ex = dit.attn_skip_softmax(q.cuda(), k.cuda(), v.cuda(), 4.0, sm_scale=sm, return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    bm = ex["bitmap"].cpu().numpy()
+    assert bm.shape[-1] == 2 and bm[0, 0, 0, 0] == 0
+    assert bool(bm[0, 0, 0, 1]) == skipped
+    assert int(ex["skipped"][0]) == int(skipped)
