@@ -1,4 +1,5 @@
 """Helpers shared by the GPU parity tests (comparison metrics, device checks)."""
+import math
 import os
 import sys
 
@@ -34,3 +35,16 @@ def dense_tolerances(got, ref):
     ma, rl = max_abs(got, ref), rel_l2(got, ref)
     assert ma <= 1e-2 and rl <= 5e-3, f"max_abs={ma:.3e} rel_l2={rl:.3e}"
     return ma, rl
+
+
+def ramp_qkv(S, step, seed, sign=1.0):
+    """Logits that change by `step` (natural units, sm_scale 1/sqrt(128) folded in) per key in
+    key order, on top of Gaussian noise: with a rising ramp every KV tile raises the row
+    maximum, so the running reference moves and the accumulators are rescaled again and again."""
+    g = torch.Generator().manual_seed(seed)
+    q = 0.3 * torch.randn(1, S, 2, 128, generator=g)
+    k = 0.3 * torch.randn(1, S, 1, 128, generator=g)
+    v = torch.randn(1, S, 1, 128, generator=g)
+    q[..., 0] = 1.0
+    k[0, :, 0, 0] = sign * step * math.sqrt(128) * torch.arange(S, dtype=torch.float32)
+    return q.bfloat16(), k.bfloat16(), v.bfloat16()

@@ -8,7 +8,7 @@ import torch
 import diffusion_transformer_attention_non_amd as dit
 from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate
 from oracle import exact_attention
-from tests._gpu_util import announce, dense_tolerances, needs_gpu, rel_l2, to_np
+from tests._gpu_util import announce, dense_tolerances, needs_gpu, ramp_qkv, rel_l2, to_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 SC = 1 / math.sqrt(128)
@@ -123,3 +123,15 @@ def test_lse_merges_two_key_halves():
     wb = torch.exp(lb - lse).transpose(1, 2)[..., None]
     merged = wa * oa + wb * ob
     assert rel_l2(to_np(merged), to_np(o)) <= 5e-3
+
+
+@pytest.mark.parametrize("step,sign", [(0.2, 1.0), (0.2, -1.0), (0.02, 1.0)])
+def test_moving_reference(step, sign):
+    """Row maxima that rise across the whole KV range (the reference moves past the slack
+    many times) or fall (every later exponential underflows towards zero)."""
+    S = 1000
+    announce(f"dense ramp step={step} sign={sign}")
+    q, k, v = ramp_qkv(S, step, seed=11, sign=sign)
+    o = _run(q, k, v, torch.float32)
+    torch.cuda.synchronize()
+    dense_tolerances(to_np(o), exact_attention(q, k, v, SC))
