@@ -8,7 +8,7 @@ import torch
 import diffusion_transformer_attention_non_amd as dit
 from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate, positional_qkv
 from oracle import skip_attention
-from tests._gpu_util import announce, needs_gpu, rel_l2, to_np
+from tests._gpu_util import announce, dense_tolerances, needs_gpu, ramp_qkv, rel_l2, to_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 SC = 1 / math.sqrt(128)
@@ -146,3 +146,30 @@ def test_threshold_boundary(delta, skipped):
     assert bm.shape[-1] == 2 and bm[0, 0, 0, 0] == 0
     assert bool(bm[0, 0, 0, 1]) == skipped
     assert int(ex["skipped"][0]) == int(skipped)
+
+
+@pytest.mark.parametrize("sign,factor", [(1.0, 4.0), (-1.0, 4.0), (-1.0, 0.5)])
+def test_moving_reference(sign, factor):
+    """Logits rising by 0.2 per key over 1,000 keys (no half can be dropped, the lazy
+    reference passes its slack on every half) or falling (each half's maximum sits about 6.4
+    under the previous one: at lambda = 4 / 1000, exp(-6.4) < lambda and every later half is
+    dropped; at lambda = 0.5 / 1000 (ln = -7.6) the second half is kept and the rest, 12.8
+    and more under the running maximum, are dropped)."""
+    announce(f"skip ramp sign={sign} factor={factor}")
+    q, k, v = ramp_qkv(1000, 0.2, seed=13, sign=sign)
+    bm, bn = dit.tile_config()
+    o, ex = dit.attn_skip_softmax(q.cuda(), k.cuda(), v.cuda(), factor, out_dtype=torch.float32,
+                                  return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    ref, skipped, ratio, rows = skip_attention(q, k, v, SC, factor, bm, bn)
+    got = ex["bitmap"].cpu().numpy().astype(bool)
+    flips = _compare_skip_sets(got, skipped, ratio, factor / q.shape[1], _log_band(q, k))[1]
+    assert int(ex["skipped"][0]) == int(got.sum())
+    if sign > 0:
+        assert not got.any()
+    elif factor == 4.0:
+        assert got[..., 1:].all()
+    else:
+        assert not got[..., 1].any() and got[..., 2:].all()
+    if flips == 0:
+        dense_tolerances(to_np(o), ref)
