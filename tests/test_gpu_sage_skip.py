@@ -9,7 +9,7 @@ import torch
 import diffusion_transformer_attention_non_amd as dit
 from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate, positional_qkv
 from oracle import sage_quantize, sage_skip_attention
-from tests._gpu_util import announce, needs_gpu, rel_l2, to_np
+from tests._gpu_util import announce, needs_gpu, ramp_qkv, rel_l2, to_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 SC = 1 / math.sqrt(128)
@@ -142,3 +142,33 @@ def test_threshold_boundary_qk16pv8(delta, skipped):
     bm = ex["bitmap"].cpu().numpy()
     assert bm.shape[-1] == 2 and not bm[0, 0, :, 0].any()
     assert np.all(bm[0, 0, :, 1] == int(skipped))
+
+
+@pytest.mark.parametrize("rec,step", [(("int8", 1, 16, 1), 0.2), (("bf16", 0, 0, 0), 0.2), (("fp8", 1, 4, 1), 0.05)])
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_moving_reference(rec, step, sign):
+    """Rising logits (no tile can be dropped; the integer reference moves every tile) and
+    falling ones (at factor 4 every tile from the third on drops, each sitting at least 9
+    log2 units under the running maximum; at step 0.2 the second drops too) through the
+    combined kernel."""
+    dt, qb, kb, vb = rec
+    announce(f"sage-skip ramp {dt} ({qb},{kb},{vb}) step={step} sign={sign}")
+    q, k, v = ramp_qkv(1000, step, seed=14, sign=sign)
+    r = dit.SageRecipe(dt, "fp8", qb, kb, vb)
+    o, ex = dit.attn_sage_skip_softmax(q.cuda(), k.cuda(), v.cuda(), r, 4.0, out_dtype=torch.float32,
+                                       return_bitmap=True, return_count=True)
+    torch.cuda.synchronize()
+    bm, _ = dit.sage_skip_tile()
+    quant = sage_quantize(q, k, v, dt, qb, kb, vb)
+    ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 4.0, bm, dit.kv_tile())
+    got = ex["bitmap"].cpu().numpy().astype(bool)
+    flips = _compare(got, skipped, ratio, 4.0 / q.shape[1])
+    assert int(ex["skipped"][0]) == int(got.sum())
+    if sign > 0:
+        assert not skipped.any() and not got.any()
+    else:
+        assert skipped[..., 2:].all()
+    r_ = rel_l2(to_np(o)[:, rows], ref)
+    assert r_ <= 3e-2, r_
+    if flips == 0 and dt != "fp8":
+        assert r_ <= 5e-3, r_
