@@ -319,6 +319,20 @@ def main():
             extra[name + "_wan"] = {"ms": ms, "tflops": F / ms / 1e9, "frac_of_peak": F / ms / 1e9 / peak, "peak": peak,
                                     "includes": "quantization + attention"}
             del wsr
+        # SAGE quantization alone (HBM-bound): algorithmic bytes = 2 B read + 1 B
+        # written per element of Q, K and V, plus the statistics pass re-reading K and V.
+        # Timed as a captured HIP graph, so the binding's host work between calls
+        # (which exceeds these few kernels' device time) stays out of the figure.
+        dit.sage_quantize(q4, k4, v4, rec, workspace=ws)
+        torch.cuda.synchronize()
+        gq = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gq):
+            dit.sage_quantize(q4, k4, v4, rec, workspace=ws)
+        ms_q = timed_calls(gq.replay, 5, torch)
+        del gq
+        qbytes = B * S * H * D * (3 + 5 + 5)
+        extra["sage_quantize_fp8_141_wan"] = {"ms": ms_q, "algorithmic_bytes": qbytes, "gbps": qbytes / ms_q / 1e6,
+                                              "frac_of_hbm_peak": qbytes / ms_q / 1e6 / HBM_GBPS}
         del q4, k4, v4, ws, o_sage
         q2, k2, v2 = generate("dense_gqa_b2_h24kv8_s8192", device=dev)
         ms = timed_calls(lambda: dit.attn_dense_bf16(q2, k2, v2), 5, torch)
