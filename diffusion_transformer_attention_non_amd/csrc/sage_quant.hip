@@ -69,6 +69,9 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(SageQuantArgs a) {
   float vmax[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int s_end = min(a.Skv, (c + 1) * kMeanChunk);
   const bool smooth = a.smooth != 0;
+  // Unrolled so that several rows' loads are in flight at once; the sums still
+  // run in token order.
+#pragma unroll 8
   for (int s = c * kMeanChunk; s < s_end; ++s) {
     float kx[8], vx[8];
     if (smooth) unpack8(ldg16(kp + (int64_t)s * a.ks[1]), kx);
