@@ -102,6 +102,7 @@ __global__ __launch_bounds__(128) void kv_finish_kernel(SageQuantArgs a) {
   const int nchunks = (a.Skv + kMeanChunk - 1) / kMeanChunk;
   const float* part = a.k_partial + ((int64_t)b * a.Hkv + g) * nchunks * kHeadDim + d;
   float tot = 0.0f;
+#pragma unroll 8   // loads run ahead; the sum keeps chunk order
   for (int c = 0; c < nchunks; ++c) tot = tot + part[(int64_t)c * kHeadDim];
   const int64_t idx = ((int64_t)b * a.Hkv + g) * kHeadDim + d;
   a.k_mean[idx] = a.smooth ? tot / (float)a.Skv : 0.0f;
