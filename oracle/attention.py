@@ -19,9 +19,14 @@ Parity status:
   sage_quantize     pinned: softmax invariance of the smoothing, round-trip
                     error bounds, absmax element -> +-QMAX, zero blocks,
                     per-block brute force on tiny inputs.
+  sage_quantize     also pinned: every per-element code against a scalar
+                    brute force (Python division rounded to binary32, round
+                    half to even, nearest-value search over the OCP E4M3 table).
   sage_attention    pinned: Q = 0 closed form, equality with exact attention
                     on exactly representable inputs with P rounding off,
-                    independence of the KV tile size with P rounding off.
+                    independence of the KV tile size with P rounding off;
+                    two-key closed forms (one tile, and one key per tile with
+                    the maximum moving); the error bound for a constant V.
   sage_skip_attention pinned: factor 0 equals sage_attention bit for bit;
                     with P rounding off, skip set and output equal
                     skip_attention on the dequantized inputs; monotone in the
@@ -43,8 +48,6 @@ import math
 import numpy as np
 
 from .codecs import E4M3_MAX, INT8_MAX, e4m3_decode, e4m3_encode, f32, int8_code, bf16_round
-
-LOG2E = 1.0 / math.log(2.0)
 
 MEAN_CHUNK = 256
 _ROW_CHUNK_ELEMS = 1 << 25
@@ -310,10 +313,12 @@ def sage_quantize(q, k, v, qk_dtype, q_block, k_block, v_block=1, v_amax=None):
 
 
 def _logits(quant, b, h, g, rows, keys, sm_scale):
-    """Log2-unit logits L_ij = log2(e) * sm_scale * <dequantized q_i, k_j> of
-    one (batch, query head), from the codes and scales of ``sage_quantize``:
-    sq(i) sk(j) <qc_i, kc_j> for SageAttention, the BF16 dot for QK16PV8, and
-    sum over 32-channel blocks of X_q X_k <qc, kc> for MXFP8."""
+    """Logits s_ij = sm_scale * <dequantized q_i, dequantized k_j> (natural
+    units) of one (batch, query head), from the codes and scales of
+    ``sage_quantize``: sq(i) sk(j) <qc_i, kc_j> for SageAttention, the BF16
+    dot for QK16PV8, and the sum over 32-channel blocks of X_q X_k <qc, kc>
+    for MXFP8.  Every dot is exact in float64 (int8 sums stay below 2**21,
+    products of E4M3 codes carry at most 8 significant bits)."""
     dt = quant["qk_dtype"]
     qc = _decode(quant["q_codes"][b, h][rows], dt)
     kc = _decode(quant["k_codes"][b, g][keys], dt)
@@ -330,7 +335,30 @@ def _logits(quant, b, h, g, rows, keys, sm_scale):
         sq = quant["q_scale"][b, h][rows // quant["q_block"]].astype(np.float64)
         sk = quant["k_scale"][b, g][keys // quant["k_block"]].astype(np.float64)
         dots = sq[:, None] * sk[None, :] * (qc @ kc.T)
-    return sm_scale * dots * LOG2E
+    return sm_scale * dots
+
+
+# How P enters BMM2.  The pages say only that both matmuls of SAGE run in low
+# precision ("TRTLLM Attention", section "SAGE quantization"; "VisualGen
+# Quantized Attention", section "Overview": BMM1 and BMM2 on narrower
+# instructions), so P, BMM2's left operand, is FP8 E4M3 like V; they give
+# neither P's scale, nor the reference it is taken against, nor how the row
+# sum is formed.  Reading taken: the plain online softmax with only BMM2's
+# operand narrowed.  The reference m is the exact running maximum of s over
+# the tiles so far; p = exp(s - m) lies in (0, 1]; BMM2 multiplies
+# p~ = E4M3(2**8 p) (2**8 keeps p's useful range inside E4M3's normal
+# binades; at most 256 < 448, so nothing saturates); the row sum, a softmax
+# statistic and not a matmul operand, adds the unrounded p.
+def _sage_tile(m, l, acc, st, vt, quantize_p, p_scale):
+    """One KV tile of the SAGE online softmax: logits ``st`` [R, n] and
+    dequantized V codes ``vt`` [n, D].  State: running maximum m, row sum l
+    (in units of p), accumulator acc (in units of p_scale * p times the V
+    codes).  Returns the updated (m, l, acc)."""
+    m2 = np.maximum(m, st.max(axis=1))
+    alpha = np.where(np.isneginf(m), 0.0, np.exp(m - m2))
+    p = np.exp(st - m2[:, None])
+    pt = e4m3_decode(e4m3_encode(p_scale * p)) if quantize_p else p_scale * p
+    return m2, alpha * l + p.sum(axis=1), alpha[:, None] * acc + pt @ vt
 
 
 def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale=256.0,
@@ -339,22 +367,20 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
 
     Both matmuls run on low-precision operands ("TRTLLM Attention", section
     "SAGE quantization"; "VisualGen Quantized Attention", section
-    "SageAttention in the TRTLLM backend").  Readings taken where the pages
-    are silent:
-      * BMM1 scale: s_ij = sm_scale * sq(i) * sk(j) * <qc_i, kc_j>, the dot
-        exact (int8 or E4M3 codes); for QK16PV8 the BF16 dot, for MXFP8 the
-        sum over 32-channel blocks of X_q X_k <qc, kc> (``_logits``).
-      * KV tiles of ``block_n`` keys in ascending order with an online
-        softmax whose reference is a power of two: in log2 units
-        L_ij = s_ij * log2(e), the reference is M = ceil(max L) over the
-        tiles so far (an integer), alpha = 2**(M_old - M), and
-        p_ij = 2**(L_ij - M), so p <= 1 and every rescale is exact.
-      * P enters BMM2 as p~ = E4M3(2**8 * p) (``quantize_p``), and the row
-        sum adds the same values BMM2 multiplies: l = alpha * l + sum_j p~_ij,
-        so the output is a convex combination of the dequantized V rows.
-      * acc_d = alpha * acc_d + sum_j p~_ij * dec(vc_jd);
-        O_id = acc_d * sv_d / l_i.
-    Returns O [B, R, Hq, D] (float64 unless ``out_dtype`` rounds it).
+    "SageAttention in the TRTLLM backend").  Steps, for each query row i:
+      * BMM1 and its scale: s_ij = sm_scale * sq(i) * sk(j) * <qc_i, kc_j>,
+        the dot exact (int8 or E4M3 codes); for QK16PV8 the BF16 dot, for
+        MXFP8 the sum over 32-channel blocks of X_q X_k <qc, kc> (``_logits``).
+      * KV tiles of ``block_n`` keys in ascending order, each updating the
+        online softmax state (``_sage_tile``): m' = max(m, tile max),
+        alpha = exp(m - m') (0 while m = -inf), p_ij = exp(s_ij - m'),
+        p~_ij = E4M3(2**8 p_ij) (``quantize_p``; 2**8 is ``p_scale``),
+        l = alpha l + sum_j p_ij (the unrounded p),
+        acc_d = alpha acc_d + sum_j p~_ij dec(vc_jd), m = m'.
+      * Epilogue (the BMM2 scale): O_id = acc_d * sv_d / (2**8 l_i).
+    With ``quantize_p`` off this is exact softmax attention on the
+    dequantized tensors.  Returns O [B, R, Hq, D] (float64 unless
+    ``out_dtype`` rounds it).
     """
     qc_all, kc_all, vc_all = quant["q_codes"], quant["k_codes"], quant["v_codes"]
     B, Hq, Sq, D = qc_all.shape
@@ -374,15 +400,9 @@ def sage_attention(quant, sm_scale, block_n, rows=None, quantize_p=True, p_scale
                 l = np.zeros(R)
                 acc = np.zeros((R, D))
                 for t0 in range(0, Skv, block_n):
-                    st = s[:, t0:t0 + block_n]
-                    m2 = np.maximum(m, np.ceil(st.max(axis=1)))
-                    alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - m2))
-                    p = np.exp2(st - m2[:, None])
-                    pq = e4m3_decode(e4m3_encode(p_scale * p)) if quantize_p else p_scale * p
-                    l = alpha * l + pq.sum(axis=1)
-                    acc = alpha[:, None] * acc + pq @ vd[t0:t0 + block_n]
-                    m = m2
-                out[b, :, h, :] = acc * sv[None, :] / l[:, None]
+                    m, l, acc = _sage_tile(m, l, acc, s[:, t0:t0 + block_n], vd[t0:t0 + block_n],
+                                           quantize_p, p_scale)
+                out[b, :, h, :] = acc * sv[None, :] / (p_scale * l[:, None])
     return _round_out(out, out_dtype)
 
 
@@ -397,19 +417,18 @@ def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, 
     Design & Test Plan", Part 1 section 4 for threshold = factor / seqlen).
     Readings taken:
       * the skip test runs on the dequantized logits of the SAGE path,
-        L_ij = log2(e) * sm_scale * sq(i) * sk(j) * <qc_i, kc_j> (log2 units,
-        so exp(M - m) < lambda reads 2**(M_L - m_L) < lambda);
+        s_ij = sm_scale * sq(i) * sk(j) * <qc_i, kc_j> (``_logits``);
       * queries in tiles of ``block_m`` rows, keys in the KV tiles of
         ``block_n`` keys of the SAGE online softmax; tile t > 0 of a query
-        tile is skipped iff every valid row i has 2**(M_it - m_i) < lambda =
-        factor / S_kv, M_it the row's largest L in the tile and m_i its exact
-        running maximum over the kept tiles (not the integer reference);
-      * a skipped tile changes nothing: not m, not the SAGE reference, not the
-        row sum, not the accumulator;
+        tile is skipped iff every valid row i has exp(M_it - m_i) < lambda =
+        factor / S_kv, M_it the row's largest s in the tile and m_i its exact
+        running maximum over the kept tiles;
+      * a skipped tile changes nothing: not m, not the softmax reference, not
+        the row sum, not the accumulator;
       * every kept tile is processed exactly as in ``sage_attention``.
     ``qtiles`` selects query tiles (default: all).  Returns (O [B, R, Hq, D],
     skipped [B, Hq, nQT, T] bool, ratio [B, Hq, nQT, T] = max_i
-    2**(M_it - m_i) with NaN at t = 0, rows).
+    exp(M_it - m_i) with NaN at t = 0, rows).
     """
     qc_all, kc_all, vc_all = quant["q_codes"], quant["k_codes"], quant["v_codes"]
     B, Hq, Sq, D = qc_all.shape
@@ -419,7 +438,7 @@ def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, 
     T = -(-Skv // block_n)
     qtiles = np.arange(nqt) if qtiles is None else np.asarray(qtiles)
     lam = float(factor) / Skv
-    log2_lam = math.log2(lam) if lam > 0 else -math.inf
+    ln_lam = math.log(lam) if lam > 0 else -math.inf
     rows = np.concatenate([np.arange(t * block_m, min(Sq, (t + 1) * block_m)) for t in qtiles])
     out = np.empty((B, len(rows), Hq, D))
     skipped = np.zeros((B, Hq, len(qtiles), T), bool)
@@ -434,7 +453,6 @@ def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, 
                 for qi, qt in enumerate(qtiles):
                     rr = np.arange(qt * block_m, min(Sq, (qt + 1) * block_m))
                     s = _logits(quant, b, h, g, rr, keys, sm_scale)
-                    m_true = np.full(len(rr), -np.inf)
                     m = np.full(len(rr), -np.inf)
                     l = np.zeros(len(rr))
                     acc = np.zeros((len(rr), D))
@@ -442,20 +460,14 @@ def sage_skip_attention(quant, sm_scale, factor, block_m, block_n, qtiles=None, 
                         st = s[:, t * block_n:(t + 1) * block_n]
                         mt = st.max(axis=1)
                         if t > 0:
-                            gap = mt - m_true
-                            ratio[b, h, qi, t] = 2.0 ** gap.max()
-                            if np.all(gap < log2_lam):
+                            gap = mt - m
+                            ratio[b, h, qi, t] = math.exp(gap.max())
+                            if np.all(gap < ln_lam):
                                 skipped[b, h, qi, t] = True
                                 continue
-                        m_true = np.maximum(m_true, mt)
-                        m2 = np.maximum(m, np.ceil(mt))
-                        alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - m2))
-                        p = np.exp2(st - m2[:, None])
-                        pq = e4m3_decode(e4m3_encode(p_scale * p)) if quantize_p else p_scale * p
-                        l = alpha * l + pq.sum(axis=1)
-                        acc = alpha[:, None] * acc + pq @ vd[t * block_n:(t + 1) * block_n]
-                        m = m2
-                    out[b, r0:r0 + len(rr), h, :] = acc * sv[None, :] / l[:, None]
+                        m, l, acc = _sage_tile(m, l, acc, st, vd[t * block_n:(t + 1) * block_n],
+                                               quantize_p, p_scale)
+                    out[b, r0:r0 + len(rr), h, :] = acc * sv[None, :] / (p_scale * l[:, None])
                     r0 += len(rr)
     return _round_out(out, out_dtype), skipped, ratio, rows
 

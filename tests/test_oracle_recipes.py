@@ -184,13 +184,15 @@ def test_tensor_wide_v_scale_from_a_slice():
 
 
 @pytest.mark.parametrize("order,block_n", [((0, 1), 2), ((0, 1), 1), ((1, 0), 1)])
-def test_p_rounding_reference_closed_form(order, block_n):
-    """Two keys with logits L = 0.9 and 0 (log2 units) and V = (1, 0) in channel 0.  The
-    reference is ceil(0.9) = 1, so P = (E4M3(2^8 * 2^-0.1), 2^7) = (240, 128) (238.86 lies
-    between the E4M3 values 224 and 240) and O_0 = 240 / 368.  A floor reference would
-    saturate the first P at 448, a 2^9 scale or row sums of the unrounded P would give
-    other values; with one key per tile the reference moves between the tiles (an exact
-    rescale by 2^-1), which changes nothing."""
+def test_p_rounding_closed_forms(order, block_n):
+    """Two keys with logits s = 0.9 ln 2 ("hot") and 0 ("cold"); V = 1 on the hot key in
+    channel 0 and on the cold key in channel 1; c = 2^-0.9.  Against the running maximum
+    0.9 ln 2, p = (1, c), and 2^8 c = 137.19 rounds to the E4M3 value 144 (between 128 and
+    144); the row sum adds the unrounded p.  So with both keys in one tile, or the hot key
+    first, O = (1, 144/256) / (1 + c).  With the cold key first its p was rounded at p = 1
+    (exact) and the later rescale by c is exact in float64: O = (1, c) / (1 + c).  A dropped
+    2^8, a row sum of the rounded p, a reference rounded up to a power of two, or a floor
+    reference would each give other values.  Without P rounding: exact softmax."""
     q = torch.zeros(1, 1, 1, 128)
     k = torch.zeros(1, 2, 1, 128)
     v = torch.zeros(1, 2, 1, 128)
@@ -198,12 +200,16 @@ def test_p_rounding_reference_closed_form(order, block_n):
     hot, cold = order
     k[0, hot, 0, 0] = 1.0
     v[0, hot, 0, 0] = 1.0
-    sm = 0.9 / math.log2(math.e)
+    v[0, cold, 0, 1] = 1.0
+    sm = 0.9 * math.log(2.0)
     quant = sage_quantize(q.bfloat16(), k.bfloat16(), v.bfloat16(), "bf16", 0, 0, 0)
-    o = sage_attention(quant, sm, block_n)
     v1 = 448.0 * float(np.float32(1.0 / 448.0))   # V = 1 dequantized: code 448 times binary32(1 / 448)
-    assert abs(o[0, 0, 0, 0] - 240.0 / 368.0 * v1) < 1e-12
-    assert np.all(o[0, 0, 0, 1:] == 0.0)
-    # without P rounding the same call is exact softmax: 2^0.9 / (2^0.9 + 1)
+    c = 2.0 ** -0.9
+    o = sage_attention(quant, sm, block_n)
+    cold_p = c if order == (1, 0) and block_n == 1 else 144.0 / 256.0
+    assert abs(o[0, 0, 0, 0] - v1 / (1 + c)) < 1e-12
+    assert abs(o[0, 0, 0, 1] - cold_p * v1 / (1 + c)) < 1e-12
+    assert np.all(o[0, 0, 0, 2:] == 0.0)
     o_exact = sage_attention(quant, sm, block_n, quantize_p=False)
     assert abs(o_exact[0, 0, 0, 0] - 2 ** 0.9 / (2 ** 0.9 + 1) * v1) < 1e-12
+    assert abs(o_exact[0, 0, 0, 1] - 1 / (2 ** 0.9 + 1) * v1) < 1e-12
