@@ -166,11 +166,14 @@ def _check_tensors(q, k, v):
 
 
 def _shape(q, k, v, o=None) -> _Shape:
+    """The C shape; without an output (quantization only) O's strides are those
+    of a contiguous [B, S_q, Hq, D] tensor."""
     B, Sq, Hq, D = q.shape
     _, Skv, Hkv, _ = k.shape
     s = _Shape(B=B, S_q=Sq, S_kv=Skv, Hq=Hq, Hkv=Hkv, D=D)
-    for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o if o is not None else q)):
+    for field, t in (("q_stride", q), ("k_stride", k), ("v_stride", v)):
         getattr(s, field)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    s.o_stride[:] = [o.stride(0), o.stride(1), o.stride(2)] if o is not None else [Sq * Hq * D, Hq * D, D]
     return s
 
 
@@ -430,10 +433,21 @@ def attention(q, k, v, *, quant: SageRecipe | None = None, skip_threshold: float
     """One DiT attention call: dense, SAGE, Skip-Softmax (when the gate
     allows), or SAGE with Skip-Softmax.
 
-    A mask is refused: this backend only serves mask-free layers.
+    ``skip_threshold`` is the threshold factor (lambda = factor / S_kv): finite
+    and >= 0, 0 meaning no skipping; anything else raises ValueError before
+    any routing.  With a ``gate``, a step whose normalized ``timestep`` is
+    above the gate's value runs without Skip-Softmax.  A mask is refused: this
+    backend only serves mask-free layers.
     """
     if attn_mask is not None:
         raise ValueError("attention masks are not supported: this path is mask-free only")
+    if skip_threshold is not None:
+        try:
+            factor = float(skip_threshold)
+        except (TypeError, ValueError):
+            raise ValueError(f"skip_threshold must be a real number, got {skip_threshold!r}") from None
+        if not (math.isfinite(factor) and factor >= 0.0):
+            raise ValueError(f"skip_threshold must be finite and >= 0, got {skip_threshold!r}")
     use_skip = skip_threshold is not None and float(skip_threshold) > 0.0
     if use_skip and gate is not None:
         if timestep is None:

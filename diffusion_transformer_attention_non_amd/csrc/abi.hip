@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <utility>
 
 #include "../../include/ditattn.h"
 #include "internal.h"
@@ -90,6 +91,28 @@ int check_shape(const attn_shape* s) {
         return fail(ATTN_ERR_BAD_LAYOUT, "%s stride[%d]=%lld must be a non-negative multiple of 8 elements",
                     names[t], i, (long long)st);
     }
+  // K and V rows must not overlap: the kernels size their buffer views from
+  // the row stride (a stride of 0, e.g. a broadcast view, would read zeros).
+  if (s->S_kv > 0 && (s->k_stride[1] < kHeadDim || s->v_stride[1] < kHeadDim))
+    return fail(ATTN_ERR_BAD_LAYOUT, "k and v stride[1] must be at least 128 elements (rows may not overlap)");
+  // O rows must not overlap: sorted by stride, every dimension of size > 1
+  // starts past the end of the ones inside it (a row is 128 elements).
+  {
+    int64_t st[3] = {s->o_stride[0], s->o_stride[1], s->o_stride[2]};
+    int64_t sz[3] = {s->B, s->S_q, s->Hq};
+    for (int i = 0; i < 3; ++i)
+      for (int j = i + 1; j < 3; ++j)
+        if (st[j] < st[i]) {
+          std::swap(st[i], st[j]);
+          std::swap(sz[i], sz[j]);
+        }
+    int64_t extent = kHeadDim;
+    for (int i = 0; i < 3; ++i) {
+      if (sz[i] <= 1) continue;
+      if (st[i] < extent) return fail(ATTN_ERR_BAD_LAYOUT, "o strides make output rows overlap");
+      extent = st[i] * sz[i];
+    }
+  }
   return ATTN_OK;
 }
 

@@ -25,24 +25,23 @@
 //         query (lane % 32) and 32 keys of the tile; the logit in log2 units
 //         is L_ij = acc_ij * sk_j * (sq_i * sm_scale * log2 e), sk = sq = 1
 //         for MXFP8 and BF16;
-//   softmax with a power-of-two reference: m' = max(m, ceil(tile max of L)),
-//         P = E4M3(2^(L - m' + 8)), l += sum P (the values BMM2 multiplies);
-//   BMM2  O^T += Vc^T P^T on E4M3 codes (v_mfma_scale_f32_32x32x64_f8f6f4,
-//         V^T codes d-major as the quantizer writes them), plus one 16x16x128
-//         selector MFMA for the row sums.
-//   O stays relative to an older integer reference mo: BMM2 takes P times
-//   2^(m - mo) through its E8M0 B scale, so moving m never touches O.  Only
-//   if m - mo would leave the safe range is O rescaled, exactly.  The four
-//   row-sum registers follow m instead (an exact power-of-two rescale when
-//   m moves).  Epilogue O = acc * sv_d * 2^(mo - m) / l (bmm2 scale).
+//   online softmax against the exact running maximum m of L: m' = max(m,
+//         tile max of L); if any row of the wavefront moved, O and the row
+//         sums are rescaled by 2^(m - m') (a wavefront-uniform branch, taken
+//         on few tiles once the maxima settle); P = E4M3(2^(L - m' + 8));
+//         the row sum l adds the unrounded fp32 p = 2^(L - m'), per lane
+//         over its 32 keys, the two lane halves combined in the epilogue;
+//   BMM2  O^T += Vc^T P^T on E4M3 codes (v_mfma_f32_32x32x64_f8f6f4, V^T
+//         codes d-major as the quantizer writes them).
+//   Epilogue O = acc * sv_d / (2^8 l) (bmm2 scale).
 //
 // Skip-Softmax (kSkip; both options in one kernel, "TRTLLM Attention",
 // section "Skip-Softmax", and "VisualGen Quantized Attention", section
 // "Interaction With Other Features"): after BMM1 of a KV tile the wavefront
 // drops the tile (no exponentials, no BMM2, no change of m) when every valid
 // row i has 2^(M_it - m_i) < lambda, M_it being the row's largest L in the
-// tile and m_i its running maximum over the tiles kept so far; lambda =
-// factor / S_kv.  The first tile is kept.
+// tile and m_i its running maximum over the tiles kept so far (the softmax
+// reference itself); lambda = factor / S_kv.  The first tile is kept.
 //
 // K (codes, or BF16 rows for QK16PV8), V^T codes and the tile's 64 K scale
 // words stream into a 4-stage LDS ring with buffer_load ... lds, three tiles
@@ -79,7 +78,6 @@ constexpr int kFmtI8 = kQkInt8, kFmtF8 = kQkFp8, kFmtMX8 = kQkMxfp8, kFmtBF16 = 
 template <int kFmt> constexpr int k_tile_bytes() { return kFmt == kFmtBF16 ? kBlockN * kHeadDim * 2 : kBlockN * kHeadDim; }
 template <int kFmt> constexpr int scale_off() { return k_tile_bytes<kFmt>() + kVTileB; }
 template <int kFmt> constexpr int stage_bytes() { return scale_off<kFmt>() + (kFmt == kFmtBF16 ? 0 : kBlockN * 4); }
-constexpr float kMaxRefGap = 64.0f;           // largest m - mo carried by the E8M0 P scale
 
 // s_waitcnt immediate for vmcnt(n) (lgkmcnt and expcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -265,29 +263,13 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  // Row sums: v_mfma_f32_16x16x128_f8f6f4 (unscaled) with B = the BMM2
-  // operand P^T (lane l: query l % 32, keys 32 (l / 32) + 0..31 = column
-  // l % 16, k group l / 16) and a 0/1 selector A (E4M3 1.0 = 0x38) whose row
-  // 0 takes k groups 0 and 2 (queries 0..15) and row 1 groups 1 and 3
-  // (queries 16..31).  Register r of lane n < 16 then holds the row sum of
-  // query 16 r + n, relative to the current reference m (P = 2^(L - m + 8)),
-  // so lrow is rescaled whenever m moves.
-  f32x4 lrow = {0.0f, 0.0f, 0.0f, 0.0f};
-  i32x8 rsel;
-  {
-    const int mrow = lane & 15, grp = lane >> 4;
-    const int one = (mrow < 2 && mrow == (grp & 1)) ? 0x38383838 : 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rsel[i] = one;
-  }
-  asm volatile("" : "+v"(rsel));   // kept in registers, not rebuilt before every use
+  // Row sum of this lane's keys (its query, its lane half), in units of
+  // 2^8 p relative to the current reference m; rescaled with O when m moves.
+  float lsum = 0.0f;
 
-  float m = kNegInf, mo = kNegInf;   // reference and O reference (integers, log2 units)
-  int bsc = 127;                      // E8M0 scale 2^(m - mo)
+  float m = kNegInf;   // running maximum of L over the (kept) tiles, log2 units
 
-  // Skip-Softmax state: exact running maximum of L over kept tiles, the
-  // wavefront's skipped-tile count and its bitmap row.
-  float mrun = kNegInf;
+  // Skip-Softmax state: the wavefront's skipped-tile count and its bitmap row.
   unsigned skipped = 0;
   const bool qvalid = q0 + l32 < Sq;
   uint8_t* bitmap_row = nullptr;
@@ -363,9 +345,9 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     // block of four or more keys per K scale (kFold) the per-key factor
     // sk * qsc is formed once per four keys and y comes from one fma with the
     // reference as it stands; if the tile then moves m, y is shifted by the
-    // (integer) change.  Otherwise the K scale (SageAttention) is applied
-    // first and y = fma(acc', qsc, 8 - m) once m is known.  (With the skip
-    // vote the folded form runs out of registers, so it keeps the other.)
+    // change.  Otherwise the K scale (SageAttention) is applied first and
+    // y = fma(acc', qsc, 8 - m) once m is known.  (With the skip vote the
+    // folded form runs out of registers, so it keeps the other.)
     constexpr bool kFold = kTokScales && kBlock4 && !kSkip;
     const float mt = m == kNegInf ? 0.0f : m;   // reference folded into y (kFold)
     if constexpr (kFold) {
@@ -409,42 +391,36 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     const float lmax = kFold ? max_halves(mx) - (8.0f - mt) : max_halves(mx) * qsc;
     if constexpr (kSkip) {
       const int t = key0 / kBlockN;
-      const bool keep = t == 0 || __any(qvalid && !(lmax - mrun < p.log2_lambda));
+      const bool keep = t == 0 || __any(qvalid && !(lmax - m < p.log2_lambda));
       if (bitmap_row != nullptr && lane == 0) bitmap_row[t] = keep ? 0 : 1;
       if (!keep) {   // wavefront-uniform: a real branch around the rest of the tile
         asm volatile("");
         ++skipped;
         return;
       }
-      mrun = fmaxf(mrun, lmax);
     }
-    // Reference update.
-    const float mnew = fmaxf(m, __builtin_ceilf(lmax));
+    // Reference update: m' = max(m, tile max).  Lanes l and l + 32 hold the
+    // same query and the same m.  alpha = 2^(m - m') is 0 on the first tile
+    // (m = -inf; O and l are still zero) and 1 on rows that did not move.
+    const float mnew = fmaxf(m, lmax);
     if (__any(mnew > m)) {
-      if (m == kNegInf) mo = mnew;   // the first tile fixes the O reference
-      // lrow follows m: scale it by 2^(m_old - m_new), exact (integers; 0 on the first tile)
-      const float fl = exp2_fast(m - mnew);
-      lrow[0] *= fl;
-      lrow[1] *= __shfl(fl, (lane & 15) + 16, 64);
-      m = mnew;
-      if (__any(m - mo > kMaxRefGap)) {
-        const float f = exp2_fast(mo - m);   // exact: the difference is an integer
-        mo = m;
+      const float alpha = exp2_fast(m - mnew);
+      lsum *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= f;
-      }
-      bsc = 127 + (int)(m - mo);
-      if constexpr (kFold) {   // y was taken against mt: shift it to the new reference (exact)
-        const float d = mt - m;
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      if constexpr (kFold) {   // y was taken against mt: shift it to the new reference
+        const float d = mt - mnew;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kb][r] += d;
       }
+      m = mnew;
     }
     // P = E4M3(2^y): byte 16 kb + r of this lane half is key 32 hh + 16 kb + r.
+    // The row sum takes the fp32 values before they are rounded.
     const float nb = 8.0f - m;
     i32x8 pf;
 #pragma unroll
@@ -453,20 +429,20 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = exp2_fast(kFold ? s[kb][r0 + j] : __builtin_fmaf(s[kb][r0 + j], qsc, nb));
+      lsum += (x[0] + x[1]) + (x[2] + x[3]);
       // The low half is written over x[0]'s own register (x[0] is dead after
       // this), so no copy of an "old" value is needed.
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __builtin_bit_cast(int, x[0]), false);
       pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
     }
-    // BMM2 and row sums, P scaled by 2^(m - mo).
+    // BMM2 and row sums.
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const i32x4 lo = *reinterpret_cast<const i32x4*>(sm + va[0] + db * 32 * kBlockN);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(sm + va[1] + db * 32 * kBlockN);
       const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, o[db], 0, 0, 0, 127, 0, bsc);
+      o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, o[db], 0, 0, 0, 127, 0, 127);
     }
-    lrow = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rsel, pf, lrow, 0, 0, 0, 127, 0, 127);
   };
 
   // ---- Tiles: stage t % 4 holds tile t.  Step t: BMM1 of tile t+1 goes out
@@ -509,9 +485,8 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
 
   // ---- Epilogue: O = O^T * sv_d / l.
   const float* svp = p.v_scale + ((int64_t)b * p.Hkv + g) * kHeadDim;
-  // O is relative to mo, l to m: O / l carries the exact factor 2^(mo - m).
-  const float l_lo = __shfl(lrow[0], l32 & 15, 64), l_hi = __shfl(lrow[1], l32 & 15, 64);
-  const float inv = exp2_fast(mo - m) / (l32 < 16 ? l_lo : l_hi);
+  // l = both lane halves' sums (lanes l and l ^ 32 hold the same query).
+  const float inv = 1.0f / (lsum + __shfl_xor(lsum, 32, 64));
   const int row = q0 + l32;
   if (row < Sq) {
     const int64_t obase = b * p.os[0] + (int64_t)row * p.os[1] + h * p.os[2];

@@ -30,7 +30,9 @@
  *   - Layout: Q is [B, S_q, Hq, D], K and V are [B, S_kv, Hkv, D], O is
  *     [B, S_q, Hq, D], each with arbitrary element strides for (b, s, h) given
  *     in attn_shape and a contiguous d axis.  Strides must be multiples of 8
- *     elements (16 bytes).  D must be 128 ([TA] "Requirements").  Query head
+ *     elements (16 bytes); K and V rows may not overlap (stride[1] >= 128
+ *     elements) and neither may the rows of O (BAD_LAYOUT otherwise; Q may
+ *     be any read-only view).  D must be 128 ([TA] "Requirements").  Query head
  *     h reads KV head h / (Hq / Hkv) ("GQA native", [DAB] backend table).
  *   - Attention is full-context and non-causal; there is no mask argument
  *     ([TA] "Requirements": a packed or mask-free path).
@@ -174,12 +176,11 @@ int sage_quantize(const void* q, const void* k, const void* v, const attn_shape*
 /* SAGE attention ([TA] "SAGE quantization": both matmuls in low precision;
  * [SSD] knob table: sage_block_sizes, bmm1_scale / bmm2_scale).
  *   Runs sage_quantize into ws, then attention on the codes:
- *   L_ij = log2(e) * sm_scale * sq_i * sk_j * <qc_i, kc_j>; online softmax
- *   over KV tiles of 64 keys in ascending order with a power-of-two reference
- *   M = ceil(running max of L) (an integer); P enters BMM2 as
- *   p~ = E4M3(2^(L - M + 8)); the row sum adds the same p~; every change of
- *   M rescales by an exact power of two; O = acc * sv_d / l.  o_dtype BF16 or
- *   FP32.  Errors as sage_quantize. */
+ *   L_ij = log2(e) * sm_scale * sq_i * sk_j * <qc_i, kc_j> (bmm1 scale);
+ *   online softmax over KV tiles of 64 keys in ascending order against the
+ *   exact running maximum m_i of L; P enters BMM2 as p~ = E4M3(2^8 p) with
+ *   p = 2^(L - m); the row sum l adds the unrounded p; O = acc * sv_d /
+ *   (2^8 l) (bmm2 scale).  o_dtype BF16 or FP32.  Errors as sage_quantize. */
 int attn_sage(const void* q, const void* k, const void* v, void* o, attn_dtype o_dtype,
               const attn_shape* shape, const attn_recipe* recipe, float sm_scale,
               void* ws, size_t ws_bytes, void* stream);

@@ -48,3 +48,36 @@ def ramp_qkv(S, step, seed, sign=1.0):
     q[..., 0] = 1.0
     k[0, :, 0, 0] = sign * step * math.sqrt(128) * torch.arange(S, dtype=torch.float32)
     return q.bfloat16(), k.bfloat16(), v.bfloat16()
+
+
+def compare_skip_sets(got, ref_skip, ratio, lam, log_band, label=""):
+    """Skipped-tile sets must be identical except on tiles whose decision sits
+    within the tie band of the threshold: |ln(ratio) - ln(lambda)| <= max(1e-6,
+    log_band), with ratio = max_i exp(M_it - m_i) from the oracle.  The 1e-6 is
+    the tie band read on the natural-log logit difference; ``log_band`` widens it
+    to the rounding bound of the kernel's own logits.  Prints the band and flip
+    counts and asserts that every flip lies inside the band."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        dist = np.abs(np.log(ratio) - math.log(lam))
+    near = (dist <= max(1e-6, log_band)) & ~np.isnan(ratio)
+    flips = got != ref_skip
+    outside = flips & ~near
+    sys.stdout.write(f"[skip-set] {label} tiles={flips.size} skipped={int(ref_skip.sum())} band={int(near.sum())} "
+                     f"flips={int(flips.sum())}\n")
+    assert not outside.any(), f"{int(outside.sum())} tiles differ outside the band (band tiles: {int(near.sum())})"
+    return int(near.sum()), int(flips.sum())
+
+
+def parallel_map(fn, items):
+    """Map ``fn`` over ``items`` on threads (the oracle's numpy work releases the
+    GIL), at most 16 at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        return list(ex.map(fn, items))
+
+
+def sample_tiles(n_tiles, count, seed=0):
+    """``count`` distinct tile indices out of ``n_tiles``: the first, the last
+    (often partial) and a seeded spread in between."""
+    inner = np.random.default_rng(seed).choice(np.arange(1, n_tiles - 1), size=count - 2, replace=False)
+    return np.unique(np.concatenate([[0, n_tiles - 1], inner]))

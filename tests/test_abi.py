@@ -236,3 +236,35 @@ def test_size_limits_rejected_before_device():
                        ws, ctypes.c_size_t(1 << 62), None)
     assert rc == INVALID
     assert b"4 GiB" in lib.attn_last_error()
+
+
+def test_overlapping_rows_rejected_before_device():
+    s = _shape()
+    s.k_stride[1] = 0                     # a broadcast K view: every row reads the same place
+    assert _dense(s) == LAYOUT
+    s = _shape()
+    s.v_stride[1] = 64
+    assert _dense(s) == LAYOUT
+    s = _shape(S=1)
+    s.k_stride[1] = 0                     # even with one key: the kernels size views from it
+    assert _dense(s) == LAYOUT
+    s = _shape()
+    s.o_stride[:] = [256 * 2 * 128, 128, 128]   # o rows of different heads collide
+    assert _dense(s) == LAYOUT
+    s = _shape()
+    s.o_stride[:] = [0, 2 * 128, 128]     # B = 1: the batch stride does not matter
+    assert _dense(s) == DEVICE
+    s = _shape()
+    s.o_stride[:] = [256 * 2 * 128, 128, 256 * 128]   # [B, H, S, D] output: fine
+    assert _dense(s) == DEVICE
+    s = _shape()
+    s.q_stride[1] = 0                     # Q is only read: a broadcast query is allowed
+    assert _dense(s) == DEVICE
+
+
+@pytest.mark.parametrize("bad", [-1.0, float("nan"), float("inf"), "x"])
+def test_attention_router_rejects_bad_threshold_before_routing(bad):
+    import torch
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)   # host tensors: nothing is launched
+    with pytest.raises(ValueError, match="skip_threshold"):
+        dit.attention(q, q, q, skip_threshold=bad)

@@ -8,7 +8,7 @@ import torch
 import diffusion_transformer_attention_non_amd as dit
 from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate
 from oracle import exact_attention
-from tests._gpu_util import announce, dense_tolerances, needs_gpu, ramp_qkv, rel_l2, to_np
+from tests._gpu_util import announce, dense_tolerances, needs_gpu, parallel_map, ramp_qkv, rel_l2, to_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 SC = 1 / math.sqrt(128)
@@ -73,6 +73,35 @@ def test_gqa_full_size_sampled_rows():
     ref = exact_attention(q, k, v, SC, rows=rows)
     got = to_np(o)[:, rows]
     dense_tolerances(got, ref)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["skip_wan_b1_h40_s75600", "sage_fp8_wan_b1_h40_s75600"])
+def test_wan_shape_sampled_rows(name):
+    """B=1, H=40, S=75,600 (the Skip-Softmax workload's spatially peaked inputs, and the
+    Gaussian ones with the K bias and outlier channels): sampled rows of the first, a middle
+    and the last (partial: 80 rows) 256-row workgroup of 4 heads against exact attention,
+    and Skip-Softmax at factor 0 bit-identical to the dense kernel."""
+    announce(f"dense wan {name} generate")
+    qd, kd, vd = generate(name, device="cuda")
+    announce(f"dense wan {name} run")
+    o = dit.attn_dense_bf16(qd, kd, vd)
+    o0 = dit.attn_skip_softmax(qd, kd, vd, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0)
+    q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
+    S = q.shape[1]
+    assert S == 75600 and (S - 256 * (S // 256)) == 80
+    rows = np.concatenate([np.arange(0, 48), np.arange(37888, 37936), np.arange(75520, 75600)])
+    heads = [0, 13, 26, 39]
+
+    def check(h):
+        sl = slice(h, h + 1)
+        ref = exact_attention(q[:, :, sl], k[:, :, sl], v[:, :, sl], SC, rows=rows)
+        return dense_tolerances(to_np(o[:, rows, sl]), ref)
+
+    for h, (ma, rl) in zip(heads, parallel_map(check, heads)):
+        print(f"{name} head {h}: max-abs {ma:.2e} rel-L2 {rl:.2e}")
 
 
 def test_empty_and_invalid_calls():

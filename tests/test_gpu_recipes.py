@@ -9,7 +9,7 @@ import torch
 import diffusion_transformer_attention_non_amd as dit
 from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate, positional_qkv
 from oracle import exact_attention, sage_attention, sage_quantize, sage_skip_attention
-from tests._gpu_util import announce, needs_gpu, ramp_qkv, rel_l2, to_np
+from tests._gpu_util import announce, compare_skip_sets, needs_gpu, ramp_qkv, rel_l2, to_np
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 SC = 1 / math.sqrt(128)
@@ -73,13 +73,10 @@ def test_skip_softmax_with_recipe_matches_oracle(rec):
     quant = sage_quantize(q, k, v, *rec)
     ref, skipped, ratio, rows = sage_skip_attention(quant, SC, 10.0, *dit.sage_skip_tile())
     got = ex["bitmap"].cpu().numpy().astype(bool)
-    lam = 10.0 / q.shape[1]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        near = np.abs(np.log2(ratio) - math.log2(lam)) <= 1e-4
-    assert not ((got != skipped) & ~near).any()
+    flips = compare_skip_sets(got, skipped, ratio, 10.0 / q.shape[1], 1e-4 * math.log(2.0), str(rec))[1]
     assert skipped.any() and int(ex["skipped"][0]) == int(got.sum())
     r_ = rel_l2(to_np(o)[:, rows], ref)
-    assert r_ <= 3e-2 and (((got != skipped) & near).any() or r_ <= 5e-3), r_
+    assert r_ <= 3e-2 and (flips or r_ <= 5e-3), r_
 
 
 @pytest.mark.parametrize("rec", [("mxfp8", 0, 0, 1), ("bf16", 0, 0, 0)])
@@ -105,15 +102,17 @@ def test_wan_shape_sampled(rec):
 
 
 @pytest.mark.parametrize("rec,step", [(("fp8", 1, 4, 1), 0.05), (("mxfp8", 0, 0, 1), 0.05),
-                                      (("int8", 1, 16, 1), 0.2), (("bf16", 0, 0, 0), 0.2)])
+                                      (("int8", 1, 16, 1), 0.2), (("bf16", 0, 0, 0), 0.2),
+                                      (("fp8", 1, 4, 1), 0.2), (("mxfp8", 0, 0, 1), 0.2)])
 @pytest.mark.parametrize("sign", [1.0, -1.0])
 def test_moving_reference(rec, step, sign):
-    """Logits rising over 1,000 keys by `step` per key (natural units): the integer reference
-    moves on every tile, the row sums follow it, and O is rescaled once the reference passes
-    the E8M0 range of the P scale (a rise of 72 log2 units at step 0.05, 288 at 0.2); or
-    falling, so P underflows through the E4M3 subnormals.  The E4M3 Q/K recipes run the
-    smaller step: their logits carry the E4M3 MFMA's accumulation error (see below), which
-    at step 0.2 reaches the output bar by itself."""
+    """Logits rising over 1,000 keys by `step` per key (natural units; 72 log2 units in all at
+    step 0.05, 288 at 0.2): the running maximum moves on every tile and O and the row sums
+    are rescaled each time; or falling, so P underflows through the E4M3 subnormals.  The
+    bar (rel-L2 3e-2 against the emulation) and the accumulation-error model below are
+    asserted wherever the model leaves room for the bar; at step 0.2 the E4M3 Q/K recipes'
+    logits reach |L| ~ 400 log2 units, where the E4M3 MFMA's accumulation error alone moves
+    the softmax weights by more than the bar allows, so only the model is asserted there."""
     dt, qb, kb, vb = rec
     announce(f"{dt} ({qb},{kb},{vb}) ramp step={step} sign={sign}")
     q, k, v = ramp_qkv(1000, step, seed=12, sign=sign)
@@ -123,8 +122,11 @@ def test_moving_reference(rec, step, sign):
     quant = sage_quantize(q, k, v, dt, qb, kb, vb)
     emu = sage_attention(quant, SC, dit.kv_tile())
     rr = rel_l2(to_np(o), emu)
-    assert rr <= 3e-2, rr                                   # the output bar against the emulation
-    assert rr <= 5e-3 + e4m3_logit_term(quant, SC), rr      # and the accumulation-error model
+    term = e4m3_logit_term(quant, SC)
+    print(f"{rec} step {step} sign {sign}: rel-L2 {rr:.3e}, model bound {5e-3 + term:.3e}")
+    assert rr <= 5e-3 + term, rr                            # the accumulation-error model
+    if term <= 2.5e-2:
+        assert rr <= 3e-2, rr                               # the output bar against the emulation
 
 
 # The E4M3 MFMA (v_mfma_*_32x32x64_f8f6f4) does not return the correctly rounded sum of its

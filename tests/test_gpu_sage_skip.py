@@ -9,21 +9,16 @@ import torch
 import diffusion_transformer_attention_non_amd as dit
 from diffusion_transformer_attention_non_amd.synth import gaussian_qkv, generate, positional_qkv
 from oracle import sage_quantize, sage_skip_attention
-from tests._gpu_util import announce, needs_gpu, ramp_qkv, rel_l2, to_np
+from tests._gpu_util import (announce, compare_skip_sets, needs_gpu, parallel_map, ramp_qkv, rel_l2,
+                             sample_tiles, to_np)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 SC = 1 / math.sqrt(128)
-NORTH_STAR_BAND = 1e-6      # |2^(M - m) - lambda| within this of the threshold is exempt
 LOG2_BAND = 1e-4            # binary32 rounding of L (a scaled int32 or fp32-accumulated dot) in log2 units
 
 
-def _compare(got, ref_skip, ratio, lam):
-    with np.errstate(divide="ignore", invalid="ignore"):
-        near = (np.abs(ratio - lam) <= NORTH_STAR_BAND) | (np.abs(np.log2(ratio) - math.log2(lam)) <= LOG2_BAND)
-    near &= ~np.isnan(ratio)
-    diff = (got != ref_skip) & ~near
-    assert not diff.any(), f"{int(diff.sum())} tiles differ outside the band (band tiles: {int(near.sum())})"
-    return int(((got != ref_skip) & near).sum())
+def _compare(got, ref_skip, ratio, lam, label=""):
+    return compare_skip_sets(got, ref_skip, ratio, lam, LOG2_BAND * math.log(2.0), label)[1]
 
 
 def _gqa(q, k, v, Hkv):
@@ -97,7 +92,9 @@ def test_invalid_threshold_rejected():
 
 
 def test_wan_shape_sampled_tiles():
-    """B=1, H=40, S=75,600 (21 x 45 x 80 grid), spatially peaked Q/K, FP8 (1, 4, 1); sampled query tiles."""
+    """B=1, H=40, S=75,600 (21 x 45 x 80 grid), spatially peaked Q/K, FP8 (1, 4, 1), factors
+    {0, 1, 10, 100}: factor 0 is attn_sage bit for bit; otherwise 8 sampled 32-row query blocks
+    (first and partial last included) of 4 heads against the combined emulation."""
     announce("sage-skip wan S=75600 H=40 generate")
     qd, kd, vd = generate("skip_wan_b1_h40_s75600", device="cuda")
     q, k, v = qd.cpu(), kd.cpu(), vd.cpu()
@@ -105,19 +102,28 @@ def test_wan_shape_sampled_tiles():
     bm, _ = dit.sage_skip_tile()
     S = q.shape[1]
     nqb = -(-S // bm)
-    heads = [0, 39]
-    qtiles = np.array([0, 1234, nqb - 1])
-    quants = {h: sage_quantize(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], "fp8", 1, 4) for h in heads}
-    for factor in (1.0, 100.0):
+    heads = [0, 13, 26, 39]
+    qtiles = sample_tiles(nqb, 8, seed=6)
+    quants = dict(zip(heads, parallel_map(
+        lambda h: sage_quantize(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], "fp8", 1, 4), heads)))
+    announce("sage-skip wan attn_sage")
+    plain = dit.attn_sage(qd, kd, vd, rec)
+    for factor in (0.0, 1.0, 10.0, 100.0):
         announce(f"sage-skip wan factor={factor}")
         o, ex = dit.attn_sage_skip_softmax(qd, kd, vd, rec, factor, return_bitmap=True, return_count=True)
         torch.cuda.synchronize()
         bitmap = ex["bitmap"].cpu().numpy().astype(bool)
         assert int(ex["skipped"][0]) == int(bitmap.sum())
-        for h in heads:
+        if factor == 0.0:
+            assert torch.equal(o, plain) and not bitmap.any()
+            continue
+
+        def check(h):
             ref, skipped, ratio, rows = sage_skip_attention(quants[h], SC, factor, bm, dit.kv_tile(), qtiles=qtiles)
-            _compare(bitmap[:, h:h + 1, qtiles], skipped, ratio, factor / S)
-            r = rel_l2(to_np(o[:, rows, h:h + 1]), ref)
+            _compare(bitmap[:, h:h + 1, qtiles], skipped, ratio, factor / S, f"factor={factor} head={h}")
+            return rel_l2(to_np(o[:, rows, h:h + 1]), ref)
+
+        for h, r in zip(heads, parallel_map(check, heads)):
             assert r <= 3e-2, (factor, h, r)
         print(f"factor {factor}: skipped fraction {bitmap.mean():.4f}")
 
@@ -147,7 +153,7 @@ def test_threshold_boundary_qk16pv8(delta, skipped):
 @pytest.mark.parametrize("rec,step", [(("int8", 1, 16, 1), 0.2), (("bf16", 0, 0, 0), 0.2), (("fp8", 1, 4, 1), 0.05)])
 @pytest.mark.parametrize("sign", [1.0, -1.0])
 def test_moving_reference(rec, step, sign):
-    """Rising logits (no tile can be dropped; the integer reference moves every tile) and
+    """Rising logits (no tile can be dropped; the running maximum moves every tile) and
     falling ones (at factor 4 every tile from the third on drops, each sitting at least 9
     log2 units under the running maximum; at step 0.2 the second drops too) through the
     combined kernel."""
