@@ -9,6 +9,7 @@ calls raise.
 Entry points (same names as the C ABI):
   attn_dense_bf16(q, k, v)                 dense BF16 attention
   sage_quantize(q, k, v, recipe)           SAGE codes and scales
+  sage_quantize_noalloc(q, k, v, recipe)   the same, statistics in a static scratch
   attn_sage(q, k, v, recipe)               SAGE attention
   attn_skip_softmax(q, k, v, factor)       Skip-Softmax attention
   attn_sage_skip_softmax(q, k, v, recipe, factor)   SAGE with Skip-Softmax
@@ -29,7 +30,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = [
-    "AttnError", "SageRecipe", "SkipGate", "attn_dense_bf16", "sage_quantize",
+    "AttnError", "SageRecipe", "SkipGate", "attn_dense_bf16", "sage_quantize", "sage_quantize_noalloc",
     "attn_sage", "attn_skip_softmax", "attn_sage_skip_softmax", "attention", "tile_config",
     "kv_tile", "sage_skip_tile", "library_path",
 ]
@@ -91,6 +92,7 @@ def _lib():
             "attn_dense_bf16": [P, P, P, P, I, SP, F, P, P],
             "attn_sage_layout_query": [SP, RP, LP],
             "sage_quantize": [P, P, P, SP, RP, P, ctypes.c_size_t, P],
+            "sage_quantize_noalloc": [P, P, P, SP, RP, P, ctypes.c_size_t, P],
             "attn_sage": [P, P, P, P, I, SP, RP, F, P, ctypes.c_size_t, P],
             "attn_skip_softmax": [P, P, P, P, I, SP, F, F, P, P, P, P],
             "attn_sage_skip_softmax": [P, P, P, P, I, SP, RP, F, F, P, P, P, ctypes.c_size_t, P],
@@ -290,6 +292,21 @@ def sage_quantize(q, k, v, recipe: SageRecipe, workspace=None):
     _check(_lib().sage_quantize(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(shape),
                                 ctypes.byref(recipe._c()), workspace.data_ptr(), workspace.numel(), _stream(q)))
     return _views(workspace, lay, q, k, recipe)
+
+
+def sage_quantize_noalloc(q, k, v, recipe: SageRecipe, out=None):
+    """sage_quantize whose statistics scratch lives in the library's static
+    device array (the C call allocates nothing).  ``out``: a uint8 device
+    buffer of at least the layout's ``scratch_off`` bytes (allocated here if
+    not given).  Returns the same views as sage_quantize."""
+    _check_tensors(q, k, v)
+    lay = _layout(q, k, v, recipe)
+    if out is None:
+        out = torch.empty(max(1, lay.scratch_off), dtype=torch.uint8, device=q.device)
+    shape = _shape(q, k, v)
+    _check(_lib().sage_quantize_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(shape),
+                                        ctypes.byref(recipe._c()), out.data_ptr(), out.numel(), _stream(q)))
+    return _views(out, lay, q, k, recipe)
 
 
 def _views(ws, lay, q, k, recipe):

@@ -266,8 +266,10 @@ void sage_layout(const attn_shape* s, const attn_recipe* r, attn_sage_layout* L)
   L->total_bytes = off;
 }
 
+// ws must hold the layout's total_bytes, or only its first scratch_off bytes
+// when the statistics live elsewhere (stats_in_ws false).
 int check_sage(const void* q, const void* k, const void* v, const attn_shape* shape, const attn_recipe* recipe,
-               void* ws, size_t ws_bytes, attn_sage_layout* L) {
+               void* ws, size_t ws_bytes, attn_sage_layout* L, bool stats_in_ws = true) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if ((rc = check_recipe(recipe))) return rc;
@@ -283,13 +285,52 @@ int check_sage(const void* q, const void* k, const void* v, const attn_shape* sh
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(ATTN_ERR_BAD_LAYOUT, "q, k, v must be 16-byte aligned");
   if (ws == nullptr) return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(ATTN_ERR_BAD_LAYOUT, "workspace must be 256-byte aligned");
-  if (ws_bytes < L->total_bytes)
-    return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %zu needed", ws_bytes, L->total_bytes);
+  const size_t need = stats_in_ws ? L->total_bytes : L->scratch_off;
+  if (ws_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %zu needed", ws_bytes, need);
   return ATTN_OK;
 }
 
+// Bytes of the quantizer's statistics (K chunk sums, then V channel maxima).
+size_t stats_bytes(const attn_shape* s) {
+  const int64_t nchunks = (s->S_kv + kMeanChunk - 1) / kMeanChunk;
+  return align256(sizeof(float) * (size_t)(s->B * s->Hkv * nchunks * kHeadDim)) +
+         align256(sizeof(unsigned) * (size_t)(s->B * s->Hkv * kHeadDim));
+}
+
+// The statistics scratch of sage_quantize_noalloc: one array per device,
+// held until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) static unsigned char scratch[kStaticScratchBytes];
+
+int static_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(ATTN_ERR_DEVICE, "no HIP device is available");
+  if (dev >= 64) return fail(ATTN_ERR_DEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(ATTN_ERR_DEVICE, "cannot resolve the static scratch array on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return ATTN_OK;
+}
+
+// Quantizer arguments for the outputs in ws; the statistics go to `stats`
+// (a region of stats_bytes) or, when it is NULL, to ws at the layout's
+// scratch offset.
 SageQuantArgs quant_args(const void* q, const void* k, const void* v, const attn_shape* s, const attn_recipe* r,
-                         void* ws, const attn_sage_layout& L) {
+                         void* ws, const attn_sage_layout& L, void* stats = nullptr) {
   SageQuantArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = q;
@@ -321,9 +362,10 @@ SageQuantArgs quant_args(const void* q, const void* k, const void* v, const attn
   a.k_scale = reinterpret_cast<float*>(w + L.k_scale_off);
   a.v_scale = reinterpret_cast<float*>(w + L.v_scale_off);
   a.k_mean = reinterpret_cast<float*>(w + L.k_mean_off);
-  a.k_partial = reinterpret_cast<float*>(w + L.scratch_off);
+  uint8_t* st = stats != nullptr ? static_cast<uint8_t*>(stats) : w + L.scratch_off;
   const int64_t nchunks = (s->S_kv + kMeanChunk - 1) / kMeanChunk;
-  a.v_absmax = reinterpret_cast<unsigned*>(w + align256(L.scratch_off + sizeof(float) * (size_t)(s->B * s->Hkv * nchunks * kHeadDim)));
+  a.k_partial = reinterpret_cast<float*>(st);
+  a.v_absmax = reinterpret_cast<unsigned*>(st + align256(sizeof(float) * (size_t)(s->B * s->Hkv * nchunks * kHeadDim)));
   a.q_mx = w + L.q_scale_off;
   a.k_mx = w + L.k_scale_off;
   return a;
@@ -497,6 +539,26 @@ int sage_quantize(const void* q, const void* k, const void* v, const attn_shape*
   if ((rc = check_ptrs(q, k, v, nullptr))) return rc;
   if ((rc = check_device_ptr(ws, "workspace"))) return rc;
   const SageQuantArgs a = quant_args(q, k, v, shape, recipe, ws, L);
+  return launched(launch_sage_quantize(a, static_cast<hipStream_t>(stream)), "SAGE quantization");
+}
+
+int sage_quantize_noalloc(const void* q, const void* k, const void* v, const attn_shape* shape,
+                          const attn_recipe* recipe, void* out, size_t out_bytes, void* stream) {
+  attn_sage_layout L;
+  int rc = check_sage(q, k, v, shape, recipe, out, out_bytes, &L, false);
+  if (rc) return rc;
+  if (shape->B == 0 || (shape->S_q == 0 && shape->S_kv == 0) || shape->Hq == 0) return ok();
+  const size_t need = stats_bytes(shape);
+  if (need > kStaticScratchBytes)
+    return fail(ATTN_ERR_WORKSPACE_TOO_SMALL,
+                "the statistics of this problem take %zu bytes, more than the %zu-byte static scratch "
+                "(B * Hkv * ceil(S_kv / 256) must stay below about %zu)",
+                need, kStaticScratchBytes, kStaticScratchBytes / (kHeadDim * sizeof(float)) - 1);
+  if ((rc = check_ptrs(q, k, v, nullptr))) return rc;
+  if ((rc = check_device_ptr(out, "out"))) return rc;
+  void* stats = nullptr;
+  if ((rc = static_scratch(&stats))) return rc;
+  const SageQuantArgs a = quant_args(q, k, v, shape, recipe, out, L, stats);
   return launched(launch_sage_quantize(a, static_cast<hipStream_t>(stream)), "SAGE quantization");
 }
 

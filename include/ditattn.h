@@ -173,6 +173,23 @@ int attn_sage_layout_query(const attn_shape* shape, const attn_recipe* recipe,
 int sage_quantize(const void* q, const void* k, const void* v, const attn_shape* shape,
                   const attn_recipe* recipe, void* ws, size_t ws_bytes, void* stream);
 
+/* sage_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same quantization, bit for bit, but the statistics scratch (K chunk
+ * sums and V channel maxima, the layout's region from scratch_off on) lives
+ * in a static device array of the library, 16 MiB per device, held until the
+ * process ends.  out receives the other regions at the layout's offsets and
+ * must hold layout.scratch_off bytes (device, 256-byte aligned); the call
+ * allocates nothing.  Problems whose statistics exceed the array,
+ * 512 * B * Hkv * (ceil(S_kv / 256) + 1) bytes or so (B * Hkv *
+ * ceil(S_kv / 256) up to about 32,000: 40 KV heads up to S_kv of about
+ * 200,000), return WORKSPACE_TOO_SMALL before any device call.  Every call on
+ * one device shares that device's array (each call clears what must start at
+ * zero): calls that overlap in time on one device race, so issue them on one
+ * stream.  Errors as sage_quantize. */
+int sage_quantize_noalloc(const void* q, const void* k, const void* v, const attn_shape* shape,
+                          const attn_recipe* recipe, void* out, size_t out_bytes, void* stream);
+
 /* SAGE attention ([TA] "SAGE quantization": both matmuls in low precision;
  * [SSD] knob table: sage_block_sizes, bmm1_scale / bmm2_scale).
  *   Runs sage_quantize into ws, then attention on the codes:

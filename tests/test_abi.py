@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert "attn_dense_bf16" in names and "attn_sage_skip_softmax" in names and len(names) == 10
+    assert "attn_dense_bf16" in names and "attn_sage_skip_softmax" in names and len(names) == 11
     out = subprocess.run(["nm", "-D", "--defined-only", dit.library_path()], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     missing = [n for n in names if n not in exported]
@@ -268,3 +268,22 @@ def test_attention_router_rejects_bad_threshold_before_routing(bad):
     q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)   # host tensors: nothing is launched
     with pytest.raises(ValueError, match="skip_threshold"):
         dit.attention(q, q, q, skip_threshold=bad)
+
+
+def test_noalloc_quantizer_limits_checked_before_device():
+    """The static statistics scratch is 16 MiB: 40 KV heads at S_kv = 300,000 (1,172 chunks of
+    256 tokens per head) need about 24 MB and are refused before any device call; the
+    output region must hold the layout's scratch_off bytes."""
+    lib = dit._lib()
+    rec = _Recipe(qk_dtype=3, v_dtype=3, q_block=1, k_block=4, v_block=1)
+    big = _shape(S=300000, Hq=40, Hkv=40)
+    assert lib.sage_quantize_noalloc(FAKE, FAKE, FAKE, ctypes.byref(big), ctypes.byref(rec), FAKE,
+                                     1 << 40, None) == WS
+    assert "static scratch" in lib.attn_last_error().decode()
+    s = _shape(S=1000)
+    lay = _Layout()
+    assert lib.attn_sage_layout_query(ctypes.byref(s), ctypes.byref(rec), ctypes.byref(lay)) == OK
+    assert lib.sage_quantize_noalloc(FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(rec), FAKE,
+                                     lay.scratch_off - 1, None) == WS
+    assert lib.sage_quantize_noalloc(FAKE, FAKE, FAKE, ctypes.byref(s), ctypes.byref(rec), FAKE,
+                                     lay.scratch_off, None) == DEVICE
