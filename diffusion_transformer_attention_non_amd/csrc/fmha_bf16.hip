@@ -409,7 +409,9 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   bf16x8 pb[2][2][2];    // dense: P^T of two halves in flight, [buffer][16-key step][qb]
   // Skip-Softmax state: exact running maxima over kept halves, the
   // wavefront's skipped-half count and its bitmap row.
-  float mrun[2] = {kNegInf, kNegInf};
+  // Lanes l and l + 32 hold the same rows, so one register carries both
+  // query blocks: lane half 0 the rows of block 0, lane half 1 those of block 1.
+  float mrun = kNegInf;
   unsigned skipped = 0;
   const int nvote = (Skv + kSkipBlockN - 1) / kSkipBlockN;
   const bool qv0 = q0 + l32 < Sq, qv1 = q0 + 32 + l32 < Sq;
@@ -427,7 +429,8 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
         // Past the first half every valid row has a finite running maximum
         // and a finite half maximum, so >= is the negation of <.  Bitwise
         // operators keep the vote free of branches.
-        const bool hot = (qv0 & (mx[0] - mrun[0] >= p.log2_lambda)) | (qv1 & (mx[1] - mrun[1] >= p.log2_lambda));
+        const float mxh = hh ? mx[1] : mx[0];
+        const bool hot = (hh ? qv1 : qv0) & (mxh - mrun >= p.log2_lambda);
         keep = u == 0 || __any(hot);
         if (bitmap_row != nullptr && lane == 0) bitmap_row[u] = keep ? 0 : 1;
         if (!keep) ++skipped;
@@ -436,8 +439,10 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
         asm volatile("");
         return false;
       }
-      mrun[0] = max_raw(mrun[0], mx[0]);
-      mrun[1] = max_raw(mrun[1], mx[1]);
+      // Keeps the compiler from hoisting the next BMM2 block's operand reads
+      // above the vote (they would stay live through it).
+      asm volatile("" ::: "memory");
+      mrun = max_raw(mrun, hh ? mx[1] : mx[0]);
     }
     if (needs_rescale(mx)) {
       rescale(mx);

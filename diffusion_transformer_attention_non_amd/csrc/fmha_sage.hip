@@ -346,9 +346,8 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     // sk * qsc is formed once per four keys and y comes from one fma with the
     // reference as it stands; if the tile then moves m, y is shifted by the
     // change.  Otherwise the K scale (SageAttention) is applied first and
-    // y = fma(acc', qsc, 8 - m) once m is known.  (With the skip vote the
-    // folded form runs out of registers, so it keeps the other.)
-    constexpr bool kFold = kTokScales && kBlock4 && !kSkip;
+    // y = fma(acc', qsc, 8 - m) once m is known.
+    constexpr bool kFold = kTokScales && kBlock4;
     const float mt = m == kNegInf ? 0.0f : m;   // reference folded into y (kFold)
     if constexpr (kFold) {
       const float nb0 = 8.0f - mt;
@@ -398,6 +397,9 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
         ++skipped;
         return;
       }
+      // Keeps the compiler from hoisting the BMM2 operand reads above the
+      // vote (they would stay live beside S through the vote).
+      asm volatile("" ::: "memory");
     }
     // Reference update: m' = max(m, tile max).  Lanes l and l + 32 hold the
     // same query and the same m.  alpha = 2^(m - m') is 0 on the first tile
