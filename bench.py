@@ -86,13 +86,65 @@ def traffic_for_current_kernel():
 
 def timed_calls(fn, n, torch):
     """Average HIP-event time (ms) of fn() over n calls on the current stream."""
+    return timed_stats(fn, n, torch)["mean_ms"]
+
+
+def timed_stats(fn, n, torch):
+    """HIP-event times (ms) of n back-to-back calls of fn() on the current
+    stream: mean, median and minimum."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     ev[0].record()
     for i in range(n):
         fn()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(n)) / n
+    ts = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+    return {"mean_ms": sum(ts) / n, "median_ms": med, "min_ms": ts[0], "launches": n}
+
+
+EXTRA_LAUNCHES = 10
+
+
+def mfma_peak_probe(torch):
+    """Matrix-core peak of each dtype on this GPU: back-to-back MFMAs on every
+    SIMD (two wavefronts each), timed with HIP events, with the shader clock the
+    waves ran at (their cycle counter against the constant-rate wall clock)."""
+    import ctypes
+    import statistics
+    path = os.path.join(ROOT, "diffusion_transformer_attention_non_amd", "libditattn_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mfma_probe_flops_per_mfma.restype = ctypes.c_double
+    lib.mfma_probe_flops_per_mfma.argtypes = [ctypes.c_int]
+    lib.mfma_probe_wall_rate_khz.restype = ctypes.c_int
+    lib.mfma_probe_launch.restype = ctypes.c_int
+    lib.mfma_probe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = 2 * cus                     # 4 wavefronts per workgroup: two per SIMD
+    waves = 4 * wgs
+    clocks = torch.zeros(4 * waves, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(waves * 64, dtype=torch.float32, device="cuda")
+    wall_khz = lib.mfma_probe_wall_rate_khz()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    for kind, name, iters, peak in ((0, "bf16", 200000, PEAK_TFLOPS["bf16"]), (1, "fp8", 100000, PEAK_TFLOPS["fp8"]),
+                                    (2, "int8", 200000, PEAK_TFLOPS["int8"])):
+        launch = lambda: lib.mfma_probe_launch(kind, wgs, iters, clocks.data_ptr(), sink.data_ptr(), stream)
+        if launch() != 0:
+            return None
+        st = timed_stats(launch, 3, torch)
+        c = clocks.view(waves, 4).cpu().numpy().astype("float64")
+        ghz = statistics.median(((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]) * wall_khz / 1e6).tolist()) if wall_khz else None
+        flops = waves * iters * 4 * lib.mfma_probe_flops_per_mfma(kind)
+        tf = flops / st["min_ms"] / 1e9
+        out[name] = {"tflops": tf, "shader_ghz": ghz, "published_peak": peak, "frac_of_published": tf / peak,
+                     "tflops_at_2p4ghz": (tf * 2.4 / ghz) if ghz else None, "ms": st["min_ms"],
+                     "mfma": {0: "v_mfma_f32_32x32x16_bf16", 1: "v_mfma_f32_32x32x64_f8f6f4",
+                              2: "v_mfma_i32_32x32x32_i8"}[kind]}
+    return out
 
 
 def cpu_baseline(budget_s, S, H, step_flops):
@@ -143,6 +195,92 @@ def cpu_baseline(budget_s, S, H, step_flops):
         "host_cpus": len(os.sched_getaffinity(0)),
         "blas_threads": blas,
     }
+
+
+def cpu_baseline_configs(gpu_ms):
+    """The oracle timed per workload beside its GPU figure, on this host's
+    cores (one BLAS thread per worker, workers over heads): the small dense
+    case and the GQA case in full; the SAGE and Skip-Softmax cases on sampled
+    64-row query tiles (first and last included) of 4 heads over the full key
+    range, extrapolated linearly to every tile of every head, plus the SAGE
+    quantizer on the full tensors."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+
+    import diffusion_transformer_attention_non_amd as dit
+    from diffusion_transformer_attention_non_amd.synth import WORKLOADS, generate
+    from oracle import exact_attention, sage_attention, sage_quantize, skip_attention
+
+    sc = 1 / math.sqrt(128)
+    workers = min(16, len(os.sched_getaffinity(0)))
+    heads_sample = [0, 13, 26, 39]
+    out = {}
+
+    def pmap(fn, items):
+        with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(fn, items))
+
+    def tiles(S, n):
+        nqt = -(-S // 64)
+        inner = np.linspace(1, nqt - 2, n - 2).round().astype(int)
+        return nqt, np.unique(np.concatenate([[0, nqt - 1], inner]))
+
+    def report(name, seconds, extrapolated, sample, flops):
+        e = {"oracle_s": seconds, "oracle_s_full_call": extrapolated, "sample": sample,
+             "oracle_gflops": flops / extrapolated / 1e9, "threads": workers}
+        if gpu_ms.get(name):
+            e["gpu_ms"] = gpu_ms[name]
+            e["gpu_speedup_over_oracle"] = extrapolated * 1e3 / gpu_ms[name]
+        out[name] = e
+
+    for name in ("dense_b1_h2_s256", "dense_gqa_b2_h24kv8_s8192"):
+        w = WORKLOADS[name]
+        q, k, v = (t.cpu() for t in generate(name, device="cuda"))
+        G = w.Hq // w.Hkv
+        jobs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+        t0 = time.perf_counter()
+        pmap(lambda bh: exact_attention(q[bh[0]:bh[0] + 1, :, bh[1]:bh[1] + 1],
+                                        k[bh[0]:bh[0] + 1, :, bh[1] // G:bh[1] // G + 1],
+                                        v[bh[0]:bh[0] + 1, :, bh[1] // G:bh[1] // G + 1], sc), jobs)
+        el = time.perf_counter() - t0
+        report(name, el, el, "every row of every head", eff_flops(w.B, w.S, w.Hq))
+
+    for name, n_tiles in (("sage_int8_b1_h40_s32768", 16), ("sage_fp8_wan_b1_h40_s75600", 8)):
+        w = WORKLOADS[name]
+        dt, _, (qb, kb, vb) = w.recipe
+        q, k, v = (t.cpu() for t in generate(name, device="cuda"))
+        t0 = time.perf_counter()
+        quants = pmap(lambda h: sage_quantize(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], dt, qb, kb, vb),
+                      range(w.Hq))
+        t_quant = time.perf_counter() - t0
+        nqt, sel = tiles(w.S, n_tiles)
+        rows = np.concatenate([np.arange(t * 64, min(w.S, t * 64 + 64)) for t in sel])
+        t0 = time.perf_counter()
+        pmap(lambda h: sage_attention(quants[h], sc, dit.kv_tile(), rows=rows), heads_sample)
+        t_att = time.perf_counter() - t0
+        scale = (nqt * w.Hq) / (len(sel) * len(heads_sample))
+        report(name, t_quant + t_att, t_quant + t_att * scale,
+               f"quantizer on all {w.Hq} heads ({t_quant:.3g} s); attention on {len(sel)} query tiles x "
+               f"{len(heads_sample)} heads ({t_att:.3g} s), x{scale:.4g} for the whole call",
+               eff_flops(w.B, w.S, w.Hq))
+        del quants
+
+    name = "skip_wan_b1_h40_s75600"
+    w = WORKLOADS[name]
+    q, k, v = (t.cpu() for t in generate(name, device="cuda"))
+    bm, bn = dit.tile_config()
+    nqt = -(-w.S // bm)
+    _, sel = tiles(w.S, 8)
+    t0 = time.perf_counter()
+    pmap(lambda h: skip_attention(q[:, :, h:h + 1], k[:, :, h:h + 1], v[:, :, h:h + 1], sc, SKIP_FACTOR, bm, bn,
+                                  qtiles=sel), heads_sample)
+    el = time.perf_counter() - t0
+    scale = (nqt * w.Hq) / (len(sel) * len(heads_sample))
+    report(name + "_factor1", el, el * scale,
+           f"{len(sel)} query tiles x {len(heads_sample)} heads ({el:.3g} s), x{scale:.4g} for the whole call",
+           eff_flops(w.B, w.S, w.Hq))
+    return out
 
 
 def profile_call(args, dit, generate, torch, dev):
@@ -269,6 +407,13 @@ def main():
                 "frac": achieved / PEAK_TFLOPS["bf16"], "traffic": traffic,
                 "kernel": "fmha_bf16_kernel", "avg_launch_ms": t_dense,
                 "algorithmic_flops_per_launch": F, "algorithmic_hbm_bytes_per_launch": 4 * B * S * H * D * 2}
+    # The low-precision path at the same shape: one attn_sage call (the
+    # quantization launches, 2 % of it, included) against the FP8 peak.
+    t_sage = timed_calls(call_sage, 3, torch)
+    roofline_sage = {"bound": "mfma", "achieved": F / t_sage / 1e9, "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                     "frac": F / t_sage / 1e9 / PEAK_TFLOPS["fp8"], "traffic": None,
+                     "kernel": "fmha_sage_kernel<E4M3, k_block 4> + SAGE quantization", "avg_call_ms": t_sage,
+                     "algorithmic_flops_per_call": F}
 
     # HBM calibration copy of a known size (also read by the counter runs).
     buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -277,7 +422,20 @@ def main():
     copy_gbps = 2 * buf.numel() / t_copy / 1e6
     del buf, dst
 
+    print("[bench] matrix-core peak probe", file=sys.stderr, flush=True)
+    probe = mfma_peak_probe(torch)
+
+    def entry(fn, flops, peak, **kw):
+        st = timed_stats(fn, EXTRA_LAUNCHES, torch)
+        e = {"ms": st["median_ms"], "min_ms": st["min_ms"], "mean_ms": st["mean_ms"], "launches": st["launches"]}
+        if flops is not None:
+            e.update(tflops=flops / st["median_ms"] / 1e9, frac_of_peak=flops / st["median_ms"] / 1e9 / peak,
+                     peak=peak)
+        e.update(kw)
+        return e
+
     extra = {}
+    c1_ms = None
     if not args.no_extra:
         print("[bench] other workloads and the factor sweep", file=sys.stderr, flush=True)
         sweep = {}
@@ -288,10 +446,11 @@ def main():
             def run_f(f=f, cnt=cnt):
                 _, ex = dit.attn_skip_softmax(q5, k5, v5, f, out=o_skip, return_count=True)
                 cnt["n"] = ex["skipped"]
-            ms = timed_calls(run_f, 2, torch)
+            e = entry(run_f, None, None)
             frac = float(cnt["n"][0]) / bitmap_total
-            sweep[str(f)] = {"ms": ms, "effective_tflops": F / ms / 1e9, "skip_fraction": frac,
-                             "algorithmic_tflops": (2 + 2 * (1 - frac)) * B * H * S * S * D / ms / 1e9}
+            e.update(effective_tflops=F / e["ms"] / 1e9, skip_fraction=frac,
+                     algorithmic_tflops=(2 + 2 * (1 - frac)) * B * H * S * S * D / e["ms"] / 1e9)
+            sweep[str(f)] = e
         extra["skip_factor_sweep_wan"] = sweep
         # SAGE FP8 (1,4,1) with Skip-Softmax on the same spatially peaked inputs
         # (quantization included); votes are 32 rows x one 64-key KV tile.
@@ -304,20 +463,20 @@ def main():
             def run_sf(f=f, cnt=cnt):
                 _, ex = dit.attn_sage_skip_softmax(q5, k5, v5, rec, f, out=o_sage, workspace=ws, return_count=True)
                 cnt["n"] = ex["skipped"]
-            ms = timed_calls(run_sf, 2, torch)
+            e = entry(run_sf, None, None)
             frac = float(cnt["n"][0]) / sage_votes
-            sweep[str(f)] = {"ms": ms, "effective_tflops": F / ms / 1e9, "skip_fraction": frac,
-                             "algorithmic_tflops": (2 + 2 * (1 - frac)) * B * H * S * S * D / ms / 1e9}
+            e.update(effective_tflops=F / e["ms"] / 1e9, skip_fraction=frac,
+                     algorithmic_tflops=(2 + 2 * (1 - frac)) * B * H * S * S * D / e["ms"] / 1e9)
+            sweep[str(f)] = e
         extra["sage_fp8_skip_factor_sweep_wan"] = sweep
         # The other FP8-BMM2 recipes at the same shape, on the SAGE workload's
         # inputs (quantization included): QK16PV8 and MXFP8 Q/K.
         for name, r in (("qk16pv8_bf16_000", dit.SageRecipe("bf16", "fp8", 0, 0, 0)),
                         ("mxfp8_001", dit.SageRecipe("mxfp8", "fp8", 0, 0, 1))):
             wsr = dit.sage_workspace(q4, k4, v4, r)
-            ms = timed_calls(lambda: dit.attn_sage(q4, k4, v4, r, out=o_sage, workspace=wsr), 3, torch)
             peak = PEAK_TFLOPS["fp8"] if r.qk_dtype == "mxfp8" else 1.0 / (0.5 / PEAK_TFLOPS["bf16"] + 0.5 / PEAK_TFLOPS["fp8"])
-            extra[name + "_wan"] = {"ms": ms, "tflops": F / ms / 1e9, "frac_of_peak": F / ms / 1e9 / peak, "peak": peak,
-                                    "includes": "quantization + attention"}
+            extra[name + "_wan"] = entry(lambda: dit.attn_sage(q4, k4, v4, r, out=o_sage, workspace=wsr), F, peak,
+                                         includes="quantization + attention")
             del wsr
         # SAGE quantization alone (HBM-bound): algorithmic bytes = 2 B read + 1 B
         # written per element of Q, K and V, plus the statistics pass re-reading K and V.
@@ -328,27 +487,31 @@ def main():
         gq = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gq):
             dit.sage_quantize(q4, k4, v4, rec, workspace=ws)
-        ms_q = timed_calls(gq.replay, 5, torch)
-        del gq
         qbytes = B * S * H * D * (3 + 5 + 5)
-        extra["sage_quantize_fp8_141_wan"] = {"ms": ms_q, "algorithmic_bytes": qbytes, "gbps": qbytes / ms_q / 1e6,
-                                              "frac_of_hbm_peak": qbytes / ms_q / 1e6 / HBM_GBPS}
+        e = entry(gq.replay, None, None)
+        e.update(algorithmic_bytes=qbytes, gbps=qbytes / e["ms"] / 1e6, frac_of_hbm_peak=qbytes / e["ms"] / 1e6 / HBM_GBPS)
+        extra["sage_quantize_fp8_141_wan"] = e
+        del gq
         del q4, k4, v4, ws, o_sage
+        q1, k1, v1 = generate("dense_b1_h2_s256", device=dev)
+        o1 = torch.empty(q1.shape, dtype=torch.float32, device=dev)
+        extra["dense_b1_h2_s256_fp32out"] = entry(lambda: dit.attn_dense_bf16(q1, k1, v1, out=o1), eff_flops(1, 256, 2),
+                                                  PEAK_TFLOPS["bf16"])
+        c1_ms = extra["dense_b1_h2_s256_fp32out"]["ms"]
+        del q1, k1, v1, o1
         q2, k2, v2 = generate("dense_gqa_b2_h24kv8_s8192", device=dev)
-        ms = timed_calls(lambda: dit.attn_dense_bf16(q2, k2, v2), 5, torch)
-        F2 = eff_flops(2, 8192, 24)
-        extra["dense_gqa_b2_h24kv8_s8192"] = {"ms": ms, "tflops": F2 / ms / 1e9,
-                                              "frac_of_peak": F2 / ms / 1e9 / PEAK_TFLOPS["bf16"]}
+        extra["dense_gqa_b2_h24kv8_s8192"] = entry(lambda: dit.attn_dense_bf16(q2, k2, v2), eff_flops(2, 8192, 24),
+                                                   PEAK_TFLOPS["bf16"])
         del q2, k2, v2
         q3, k3, v3 = generate("sage_int8_b1_h40_s32768", device=dev)
         rec3 = dit.SageRecipe("int8", "fp8", 1, 16, 1)
         ws3 = dit.sage_workspace(q3, k3, v3, rec3)
-        ms = timed_calls(lambda: dit.attn_sage(q3, k3, v3, rec3, workspace=ws3), 3, torch)
-        ms_q = timed_calls(lambda: dit.sage_quantize(q3, k3, v3, rec3, workspace=ws3), 3, torch)
         F3 = eff_flops(1, 32768, 40)
-        # respective peak for int8 BMM1 + fp8 BMM2: time = (F/2)/P_int8 + (F/2)/P_fp8
-        extra["sage_int8_b1_h40_s32768"] = {"ms": ms, "quantize_ms": ms_q, "tflops": F3 / ms / 1e9,
-                                            "frac_of_peak": F3 / ms / 1e9 / PEAK_TFLOPS["int8"]}
+        # respective peak for int8 BMM1 + fp8 BMM2: time = (F/2)/P_int8 + (F/2)/P_fp8 (both 5.0 P)
+        e = entry(lambda: dit.attn_sage(q3, k3, v3, rec3, workspace=ws3), F3, PEAK_TFLOPS["int8"],
+                  includes="quantization + attention")
+        e["quantize_ms"] = timed_stats(lambda: dit.sage_quantize(q3, k3, v3, rec3, workspace=ws3), 3, torch)["median_ms"]
+        extra["sage_int8_b1_h40_s32768"] = e
         del q3, k3, v3, ws3
 
     result = {
@@ -368,12 +531,21 @@ def main():
                    "B": B, "S": S, "H": H, "D": D, "skip_factor": SKIP_FACTOR, "gate": {"D": GATE_D, "t": GATE_T}},
         "modes": modes,
         "roofline": roofline,
+        "roofline_sage_fp8": roofline_sage,
+        "mfma_peak_probe": probe,
         "hbm_copy_gbps": copy_gbps,
         "extra": extra,
     }
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, S, H, step_flops)
+        if not args.no_extra:
+            print("[bench] CPU oracle per workload", file=sys.stderr, flush=True)
+            gpu_ms = {"dense_b1_h2_s256": c1_ms, "dense_gqa_b2_h24kv8_s8192": extra["dense_gqa_b2_h24kv8_s8192"]["ms"],
+                      "sage_int8_b1_h40_s32768": extra["sage_int8_b1_h40_s32768"]["ms"],
+                      "sage_fp8_wan_b1_h40_s75600": per_call["sage_fp8_141"],
+                      "skip_wan_b1_h40_s75600_factor1": per_call["skip_bf16_factor1"]}
+            result["cpu_baseline_per_workload"] = cpu_baseline_configs(gpu_ms)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libditattn.so")
 SOURCES = ["abi.hip", "fmha_bf16.hip", "fmha_sage.hip", "sage_quant.hip"]
+# The benchmark's matrix-core peak probe: its own shared object, outside the library's interface.
+PROBE_LIB = os.path.join(PKG, "libditattn_probe.so")
+PROBE_SOURCES = ["mfma_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -53,20 +56,27 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source for gfx950 and link libditattn.so next to this file."""
-    obj_dir = os.path.join(ROOT, "_build")
-    os.makedirs(obj_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source for gfx950 and link libditattn.so (and the
+    benchmark's probe library) next to this file."""
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, obj_dir), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
