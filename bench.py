@@ -514,6 +514,25 @@ def main():
         extra["sage_int8_b1_h40_s32768"] = e
         del q3, k3, v3, ws3
 
+    # The step mixes bf16 and fp8 calls: its share of the blended peak is the
+    # time the three calls would take at their own peaks over the step time.
+    ideal_ms = (F / PEAK_TFLOPS["bf16"] + F / PEAK_TFLOPS["fp8"] + F / PEAK_TFLOPS["bf16"]) / 1e9
+    sweep_bf16 = extra.get("skip_factor_sweep_wan", {})
+    sweep_sage = extra.get("sage_fp8_skip_factor_sweep_wan", {})
+    targets = {
+        "dense_bf16_60pct_of_peak": {"measured": modes["dense_bf16"]["frac_of_peak"], "met": modes["dense_bf16"]["frac_of_peak"] >= 0.6},
+        "sage_fp8_50pct_of_peak": {"measured": modes["sage_fp8_141"]["frac_of_peak"], "met": modes["sage_fp8_141"]["frac_of_peak"] >= 0.5},
+    }
+    if sweep_bf16:
+        sp = sweep_bf16["0.0"]["ms"] / sweep_bf16["100.0"]["ms"]
+        targets["skip_bf16_factor100_faster_than_dense"] = {"measured_speedup": sp, "met": sp > 1.0}
+    if sweep_sage:
+        sp = sweep_sage["0.0"]["ms"] / sweep_sage["100.0"]["ms"]
+        targets["sage_skip_factor100_faster_than_sage"] = {"measured_speedup": sp, "met": sp > 1.0}
+    if "sage_int8_b1_h40_s32768" in extra:
+        fr = extra["sage_int8_b1_h40_s32768"]["frac_of_peak"]
+        targets["sage_int8_50pct_of_peak"] = {"measured": fr, "met": fr >= 0.5}
+
     result = {
         "metric": "effective attention TFLOPS + % MFMA peak at S=75,600 H=40 D=128",
         "value": step_flops / (ms_step / 1e3) / 1e12,
@@ -529,6 +548,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "wan_b1_h40_s75600_d128: dense bf16 + sage fp8 (1,4,1) + skip-softmax bf16 factor 1",
                    "B": B, "S": S, "H": H, "D": D, "skip_factor": SKIP_FACTOR, "gate": {"D": GATE_D, "t": GATE_T}},
+        "frac_of_blended_peak": ideal_ms / ms_step,
+        "targets": targets,
         "modes": modes,
         "roofline": roofline,
         "roofline_sage_fp8": roofline_sage,

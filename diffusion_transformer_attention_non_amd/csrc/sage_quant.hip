@@ -264,46 +264,58 @@ __global__ __launch_bounds__(256) void qk_quant_kernel(SageQuantArgs a) {
   }
 }
 
-// V codes, transposed.  Workgroup = 64 tokens x 128 channels of one
-// (b, kv head): coalesced 16-byte reads of V rows, E4M3 codes staged in LDS
-// as [d][token], then written as 64-byte rows of v_codes[b, g, d, :].
+// V codes, transposed.  Workgroup = 128 tokens x 128 channels of one
+// (b, kv head).  Thread t covers channels 8 (t % 16) + 0..7 of tokens
+// 4 (t / 16) + 0..3 (plus 64 in the second pass): 16-byte reads of V rows,
+// and per channel the codes of its four tokens form one 32-bit word of the
+// [channel][token] LDS tile.  The tile leaves as 128-byte rows (whole cache
+// lines) of v_codes[b, g, d, :].  Tokens at or past S_kv get zero codes.
+constexpr int kVqTokens = 128;
+constexpr int kVqPitch = kVqTokens + 16;   // bytes per LDS row (16-byte aligned rows)
+
 __global__ __launch_bounds__(256) void v_quant_kernel(SageQuantArgs a) {
-  __shared__ uint8_t tile[kHeadDim][64 + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim * kVqPitch];
   const int g = blockIdx.y, b = blockIdx.z;
-  const int s0 = blockIdx.x * 64;
+  const int s0 = blockIdx.x * kVqTokens;
   const int tid = threadIdx.x;
-  const int d0 = 8 * (tid & 15);
+  const int cg = tid & 15, tg = tid >> 4;
+  const int d0 = 8 * cg;
   const bf16_t* vp = static_cast<const bf16_t*>(a.v) + b * a.vs[0] + g * a.vs[2] + d0;
   const float* sv = a.v_scale + ((int64_t)b * a.Hkv + g) * kHeadDim + d0;
   float scale[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) scale[j] = sv[j];
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int tl = 16 * pass + (tid >> 4);
-    const int s = s0 + tl;
-    float x[8];
-    if (s < a.Skv) {
-      unpack8(ldg16(vp + (int64_t)s * a.vs[1]), x);
-    } else {
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t0 = 64 * pass + 4 * tg;   // first of this thread's four tokens within the tile
+    float x[4][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int s = s0 + t0 + i;
+      if (s < a.Skv) {
+        unpack8(ldg16(vp + (int64_t)s * a.vs[1]), x[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[i][j] = 0.0f;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const uint32_t pr = e4m3_pair(x[j] / scale[j], x[j + 1] / scale[j + 1]);
-      tile[d0 + j][tl] = (uint8_t)(pr & 0xFF);
-      tile[d0 + j + 1][tl] = (uint8_t)(pr >> 8);
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t lo = e4m3_pair(x[0][j] / scale[j], x[1][j] / scale[j]);
+      const uint32_t hi = e4m3_pair(x[2][j] / scale[j], x[3][j] / scale[j]);
+      *reinterpret_cast<uint32_t*>(&tile[(d0 + j) * kVqPitch + t0]) = lo | hi << 16;
     }
   }
   __syncthreads();
   uint8_t* out = a.v_codes + ((int64_t)b * a.Hkv + g) * kHeadDim * a.s_pad + s0;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int idx = pass * 256 + tid;   // 512 chunks of 16 bytes
-    const int d = idx >> 2, part = idx & 3;
-    const uint4 w = *reinterpret_cast<const uint4*>(&tile[d][16 * part]);
-    *reinterpret_cast<uint4*>(out + (int64_t)d * a.s_pad + 16 * part) = w;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int idx = pass * 256 + tid;   // 1024 chunks of 16 bytes: channel idx / 8, part idx % 8
+    const int d = idx >> 3, part = idx & 7;
+    if (s0 + 16 * part < a.s_pad) {     // s_pad is a multiple of 64: the last tile may be half
+      const uint4 w = *reinterpret_cast<const uint4*>(&tile[d * kVqPitch + 16 * part]);
+      *reinterpret_cast<uint4*>(out + (int64_t)d * a.s_pad + 16 * part) = w;
+    }
   }
 }
 
@@ -326,7 +338,8 @@ hipError_t launch_sage_quantize(const SageQuantArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(qk_quant_kernel<false>, dim3(groups, a.Hq + a.Hkv, a.B), dim3(256), 0, stream, a);
   else if (a.qk_fmt == kQkMxfp8)
     hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)(a.s_pad / 16), a.Hq + a.Hkv, a.B), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(v_quant_kernel, dim3((unsigned)(a.s_pad / 64), a.Hkv, a.B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(v_quant_kernel, dim3((unsigned)((a.s_pad + kVqTokens - 1) / kVqTokens), a.Hkv, a.B), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
