@@ -62,6 +62,20 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t lds_addr,
       : "memory", "m0");
 }
 
+// As buffer_load_lds16 with the LDS address given as base + offset, added in
+// the instruction stream: only the base needs to stay in a register across a
+// loop, the offset (a constant at the call site) is rematerialized.
+__device__ __forceinline__ void buffer_load_lds16_at(i32x4 rsrc, uint32_t lds_base, uint32_t lds_off,
+                                                     uint32_t voffset) {
+  asm volatile(
+      "s_add_u32 m0, %0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds"
+      :
+      : "s"(lds_base), "s"(lds_off), "v"(voffset), "s"(rsrc)
+      : "memory", "m0", "scc");
+}
+
 // As buffer_load_lds16 with 4 bytes per lane: LDS bytes [lds_addr + 4 l, lds_addr + 4 l + 4).
 __device__ __forceinline__ void buffer_load_lds4(i32x4 rsrc, uint32_t lds_addr, uint32_t voffset) {
   asm volatile(

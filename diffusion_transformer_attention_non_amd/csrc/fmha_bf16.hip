@@ -174,12 +174,10 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   const uint32_t wave_slot = (uint32_t)__builtin_amdgcn_readfirstlane(1024 * wave);
   auto issue_loads = [&](auto s, int t) __attribute__((always_inline)) {
     const uint32_t tk = (uint32_t)t * kBlockN * kstride, tv = (uint32_t)t * kBlockN * vstride;
-    const uint32_t kd = lds_addr(kst(s)) + wave_slot;
-    const uint32_t vd = lds_addr(vst(s)) + wave_slot;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buffer_load_lds16(krsrc, kd + 4096 * i, koff[i] + tk);
+    for (int i = 0; i < 4; ++i) buffer_load_lds16_at(krsrc, wave_slot, lds_addr(kst(s)) + 4096 * i, koff[i] + tk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buffer_load_lds16(vrsrc, vd + 4096 * i, voff[i] + tv);
+    for (int i = 0; i < 4; ++i) buffer_load_lds16_at(vrsrc, wave_slot, lds_addr(vst(s)) + 4096 * i, voff[i] + tv);
   };
 
   // ---- LDS read addresses (lane constants; the rest is immediate).
@@ -481,16 +479,16 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       // Tile j+3 goes into the stage tile j-1 used (every wavefront is past
       // it now): K loads ride in the first block, V loads in the second.
       const uint32_t tk = (uint32_t)(j + 3) * kBlockN * kstride, tv = (uint32_t)(j + 3) * kBlockN * vstride;
-      const uint32_t kd = lds_addr(kst(IC<(S + 3) & 3>{})) + wave_slot;
-      const uint32_t vd = lds_addr(vst(IC<(S + 3) & 3>{})) + wave_slot;
+      const uint32_t kd = lds_addr(kst(IC<(S + 3) & 3>{}));   // plus wave_slot, added at each load
+      const uint32_t vd = lds_addr(vst(IC<(S + 3) & 3>{}));
       bmm1_block(ks, 1, sb[1], [&](int t) __attribute__((always_inline)) {
         p_valu(sb[0], pb[0], t);
-        if ((t & 3) == 2) buffer_load_lds16(krsrc, kd + 4096 * (t >> 2), koff[t >> 2] + tk);
+        if ((t & 3) == 2) buffer_load_lds16_at(krsrc, wave_slot, kd + 4096 * (t >> 2), koff[t >> 2] + tk);
       });
       mask_half(sb[1], key0 + 32);
       auto qv_odd = [&](int t) __attribute__((always_inline)) {
         q_valu(sb[1], pb[1], t);
-        if ((t & 3) == 2) buffer_load_lds16(vrsrc, vd + 4096 * (t >> 2), voff[t >> 2] + tv);
+        if ((t & 3) == 2) buffer_load_lds16_at(vrsrc, wave_slot, vd + 4096 * (t >> 2), voff[t >> 2] + tv);
       };
       if (!kSkip || keep_b[0])
         bmm2_block(vs, 0, pb[0], qv_odd);
