@@ -14,11 +14,13 @@
 //   kFmtBF16 Q and K read as BF16 from the inputs (QK16PV8).
 //
 // Work decomposition
-//   workgroup = 8 wavefronts = 256 query rows of one (batch, query head), two
-//   wavefronts per SIMD; each wavefront owns 32 query rows and walks all KV
-//   tiles of 64 keys.  While one wavefront of a SIMD issues its E4M3 MFMAs the
-//   other runs its softmax VALU work at full rate (a single wavefront issues
-//   VALU at half rate while its own E4M3 MFMA executes).  Per tile:
+//   workgroup = 12 wavefronts = 384 query rows of one (batch, query head),
+//   three wavefronts per SIMD (at most 168 VGPRs each); each wavefront owns
+//   32 query rows and walks all KV tiles of 64 keys.  While one wavefront of
+//   a SIMD issues its MFMAs the other two run softmax VALU work (a single
+//   wavefront issues VALU at half rate while its own E4M3 MFMA executes), so
+//   the SIMD's scheduler, not a fixed interleave in the code, overlaps the
+//   two.  Per tile:
 //   BMM1  S^T = Kc Qc^T on int8 (v_mfma_i32_32x32x32_i8, exact int32), OCP
 //         E4M3 (v_mfma_scale_f32_32x32x64_f8f6f4, MXFP8 with its block
 //         scales) or BF16 (v_mfma_f32_32x32x16_bf16); each lane holds one
@@ -45,7 +47,8 @@
 //
 // K (codes, or BF16 rows for QK16PV8), V^T codes and the tile's 64 K scale
 // words stream into a 4-stage LDS ring with buffer_load ... lds, three tiles
-// ahead (out-of-range reads are zero); one barrier per tile.  LDS layouts
+// ahead (out-of-range reads are zero), issued by the first eight wavefronts
+// (one load round each); one barrier per tile.  LDS layouts
 // (16-byte chunks, XOR-swizzled so that the 16 lanes an LDS cycle serves, 16
 // consecutive rows at one logical chunk, hit 16 distinct 16-byte slots of the
 // 64 four-byte banks):
@@ -68,8 +71,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kSageWaves = kWavesPerWG;
+constexpr int kSageWaves = 12;                // three wavefronts per SIMD
+constexpr int kSageLoaders = 8;               // the first eight issue the tile loads
 constexpr int kSageWaveRows = kWaveRows;   // 32 query rows per wavefront
+constexpr int kSageBlockM = kSageWaveRows * kSageWaves;   // query rows per workgroup
 constexpr int kVTileB = kHeadDim * kBlockN;   // 8 KB of V^T codes
 constexpr int kLoadsPerTile = 3;              // per wavefront: K, V and scales (BF16: 2 K, 1 V)
 
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     else if constexpr (S == 2) return st2; else return st3;
   };
 
-  const int nqt = (p.Sq + kBlockM - 1) / kBlockM;
+  const int nqt = (p.Sq + kSageBlockM - 1) / kSageBlockM;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = wg % nqt;
   const int bh = wg / nqt;
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int q0 = qt * kBlockM + wave * kSageWaveRows;
+  const int q0 = qt * kSageBlockM + wave * kSageWaveRows;
   const int Sq = p.Sq, Skv = p.Skv;
   const int64_t s_pad = p.s_pad;
   const int nkt = (Skv + kBlockN - 1) / kBlockN;
@@ -178,7 +183,8 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
 
   // ---- Loads.  Round R (0..7) of a tile's K covers LDS rows 8R..8R+7 and
   // of its V^T rows 16R..16R+15; wavefront w issues round w of each, plus the
-  // 64 scales (every wavefront writes the same 256 bytes).
+  // 64 scales (every loading wavefront writes the same 256 bytes); wavefronts
+  // 8..11 issue no loads.
   const uint8_t* vg = p.v_codes + ((int64_t)b * p.Hkv + g) * kHeadDim * s_pad;
   const i32x4 vrsrc = make_rsrc(vg, (uint32_t)(s_pad * kHeadDim));
   const int vrow = 16 * wave + (lane >> 2);
@@ -223,6 +229,7 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     sstep = (uint32_t)(4 * kBlockN);
   }
   auto issue_loads = [&](uint32_t sbase, int t) __attribute__((always_inline)) {
+    if (wave_slot >= 1024u * kSageLoaders) return;   // scalar branch: wave_slot is uniform
     if constexpr (kBf16) {
       const uint32_t tk = (uint32_t)t * kBlockN * kstride_b;
       buffer_load_lds16(krsrc, sbase + 2 * wave_slot, koff[0] + tk);
@@ -447,38 +454,33 @@ __global__ __launch_bounds__(kSageWaves * 64, 1) void fmha_sage_kernel(FmhaSageA
     }
   };
 
-  // ---- Tiles: stage t % 4 holds tile t.  Step t: BMM1 of tile t+1 goes out
-  // first, so its MFMAs run under the softmax VALU work of tile t; then BMM2
-  // of tile t.  Tiles t+2 and t+3 are in flight meanwhile.
-  f32x16 sA[2], sB[2];
+  // ---- Tiles: stage t % 4 holds tile t.  Step t: softmax and BMM2 of tile
+  // t, then BMM1 of tile t+1 (its MFMAs run under the other wavefronts of the
+  // SIMD); tiles t+2 and t+3 are in flight meanwhile.
+  f32x16 sA[2];
   issue_loads(lds_addr(st0), 0);
   issue_loads(lds_addr(st1), 1);
   issue_loads(lds_addr(st2), 2);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));   // tile 0 landed
   wg_barrier();
   bmm1(st0, sA);
-  auto iteration = [&](auto s_c, int t, f32x16 (&scur)[2], f32x16 (&snext)[2]) __attribute__((always_inline)) {
+  auto iteration = [&](auto s_c, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerTile));   // tile t+1 landed (t+2 may be in flight)
     wg_barrier();   // tiles t, t+1 visible to all; every wavefront is past tile t-1
     issue_loads(lds_addr(stage(IC<(S + 3) & 3>{})), t + 3);
     // Past the last tile the next stage holds zeros; that S is never used.
-    if (wave < kSageWaves / 2) {   // first wavefront of each SIMD: MFMA work first
-      bmm1(stage(IC<(S + 1) & 3>{}), snext);
-      softmax_bmm2(stage(IC<S>{}), scur, t * kBlockN);
-    } else {                       // second: VALU work first, so the two alternate
-      softmax_bmm2(stage(IC<S>{}), scur, t * kBlockN);
-      bmm1(stage(IC<(S + 1) & 3>{}), snext);
-    }
+    softmax_bmm2(stage(IC<S>{}), sA, t * kBlockN);
+    bmm1(stage(IC<(S + 1) & 3>{}), sA);
   };
   for (int t = 0;; t += 4) {
-    iteration(IC<0>{}, t, sA, sB);
+    iteration(IC<0>{}, t);
     if (t + 1 >= nkt) break;
-    iteration(IC<1>{}, t + 1, sB, sA);
+    iteration(IC<1>{}, t + 1);
     if (t + 2 >= nkt) break;
-    iteration(IC<2>{}, t + 2, sA, sB);
+    iteration(IC<2>{}, t + 2);
     if (t + 3 >= nkt) break;
-    iteration(IC<3>{}, t + 3, sB, sA);
+    iteration(IC<3>{}, t + 3);
     if (t + 4 >= nkt) break;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -522,7 +524,7 @@ void launch_fmt(const FmhaSageArgs& a, dim3 grid, dim3 block, hipStream_t stream
 }  // namespace
 
 hipError_t launch_fmha_sage(const FmhaSageArgs& a, hipStream_t stream) {
-  const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
+  const int64_t nqt = (a.Sq + kSageBlockM - 1) / kSageBlockM;
   const int64_t nwg = nqt * a.Hq * a.B;
   if (nwg <= 0) return hipSuccess;
   const dim3 grid((unsigned)nwg), block(kSageWaves * 64);
