@@ -250,15 +250,26 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4,
                                    5, 6, 7);
   };
+  // Fragment rings: the fragment of step s sits in slot s % (kPrefetch + 1).
+  // A block reads its own fragments kPrefetch steps ahead, and in its last
+  // kPrefetch steps the first ones of the block after it (next(i) reads
+  // fragment i of that block), so no block starts by waiting on LDS.  The
+  // block after a BMM1 block is a BMM2 block and vice versa, so next() never
+  // writes a slot of the ring the current block still reads.
+  bf16x8 kfr[kPrefetch + 1], vfr[kPrefetch + 1];
+  auto kpre = [&](const uint8_t* ks, int kb) __attribute__((always_inline)) {
+    return [&kfr, &kfrag, ks, kb](int i) __attribute__((always_inline)) { kfr[i] = kfrag(ks, kb, i); };
+  };
+  auto vpre = [&](const uint8_t* vs, int half) __attribute__((always_inline)) {
+    return [&vfr, &vfrag, vs, half](int i) __attribute__((always_inline)) { vfr[i] = vfrag(vs, half, i); };
+  };
   // 16 MFMA slots of BMM1 (half kb of K stage ks into sdst); valu(t) runs after slot t's MFMA.
-  auto bmm1_block = [&](const uint8_t* ks, int kb, f32x16 (&sdst)[2], auto&& valu) __attribute__((always_inline)) {
-    bf16x8 kfr[kPrefetch + 1];
-#pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) kfr[i] = kfrag(ks, kb, i);
+  auto bmm1_block = [&](const uint8_t* ks, int kb, f32x16 (&sdst)[2], auto&& valu, auto&& next) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int ds = t >> 1, qb = t & 1;
       if (qb == 0 && ds + kPrefetch < 8) kfr[(ds + kPrefetch) % (kPrefetch + 1)] = kfrag(ks, kb, ds + kPrefetch);
+      if (qb == 0 && ds + kPrefetch >= 8) next(ds + kPrefetch - 8);
       if (ds == 0) {
         f32x16 z;
 #pragma unroll
@@ -272,15 +283,13 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     }
   };
   // 16 MFMA slots of BMM2 (O^T += V^T P^T for half `half` of V stage vs).
-  auto bmm2_block = [&](const uint8_t* vs, int half, const bf16x8 (&pin)[2][2], auto&& valu) __attribute__((always_inline)) {
-    bf16x8 vfr[kPrefetch + 1];
-#pragma unroll
-    for (int i = 0; i < kPrefetch; ++i) vfr[i] = vfrag(vs, half, i);
+  auto bmm2_block = [&](const uint8_t* vs, int half, const bf16x8 (&pin)[2][2], auto&& valu, auto&& next) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int step = t >> 1, qb = t & 1;
       const int s2 = step >> 2, db = step & 3;
       if (qb == 0 && step + kPrefetch < 8) vfr[(step + kPrefetch) % (kPrefetch + 1)] = vfrag(vs, half, step + kPrefetch);
+      if (qb == 0 && step + kPrefetch >= 8) next(step + kPrefetch - 8);
       o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[step % (kPrefetch + 1)], pin[s2][qb], o[db][qb], 0, 0, 0);
       if ((t & 3) == 3) {
         const int rq = (t >> 2) & 1, rs = t >> 3;
@@ -290,10 +299,12 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       fence();
     }
   };
-  // The VALU work of a Q block without its MFMAs (the half before was skipped).
-  auto valu_block = [&](auto&& valu) __attribute__((always_inline)) {
+  // The VALU work of a Q block without its MFMAs (the half before was
+  // skipped); it still reads the next block's first fragments.
+  auto valu_block = [&](auto&& valu, auto&& next) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
+      if ((t & 1) == 0 && (t >> 1) + kPrefetch >= 8) next((t >> 1) + kPrefetch - 8);
       valu(t);
       fence();
     }
@@ -453,7 +464,13 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     // S of half 0 (tile 0), then its Q-block VALU work with no BMM2 to pair with.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerTile));
     wg_barrier();
-    bmm1_block(sK0, 0, sb[0], [](int) {});
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) kpre(sK0, 0)(i);
+    // The next block is BMM1 too, on the same K ring: its first fragments
+    // are read once this block is done with the ring.
+    bmm1_block(sK0, 0, sb[0], [](int) {}, [](int) {});
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) kpre(sK0, 1)(i);
     mask_half(sb[0], 0);
 #pragma unroll
     for (int t = 0; t < 16; ++t) q_valu(sb[0], pb[0], t);
@@ -484,24 +501,27 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       bmm1_block(ks, 1, sb[1], [&](int t) __attribute__((always_inline)) {
         p_valu(sb[0], pb[0], t);
         if ((t & 3) == 2) buffer_load_lds16_at(krsrc, wave_slot, kd + 4096 * (t >> 2), koff[t >> 2] + tk);
-      });
+      }, vpre(vs, 0));
       mask_half(sb[1], key0 + 32);
       auto qv_odd = [&](int t) __attribute__((always_inline)) {
         q_valu(sb[1], pb[1], t);
         if ((t & 3) == 2) buffer_load_lds16_at(vrsrc, wave_slot, vd + 4096 * (t >> 2), voff[t >> 2] + tv);
       };
       if (!kSkip || keep_b[0])
-        bmm2_block(vs, 0, pb[0], qv_odd);
+        bmm2_block(vs, 0, pb[0], qv_odd, kpre(kst(IC<(S + 1) & 3>{}), 0));
       else
-        valu_block(qv_odd);
+        valu_block(qv_odd, kpre(kst(IC<(S + 1) & 3>{}), 0));
       keep_b[1] = q_check(sb[1], pb[1], 2 * j + 1);
-      bmm1_block(kst(IC<(S + 1) & 3>{}), 0, sb[0], [&](int t) __attribute__((always_inline)) { p_valu(sb[1], pb[1], t); });
+      bmm1_block(kst(IC<(S + 1) & 3>{}), 0, sb[0], [&](int t) __attribute__((always_inline)) { p_valu(sb[1], pb[1], t); },
+                 vpre(vs, 1));
       mask_half(sb[0], key0 + kBlockN);
       auto qv_even = [&](int t) __attribute__((always_inline)) { q_valu(sb[0], pb[0], t); };
+      // The next step's first block is BMM1 of the same tile's second half
+      // (already resident: the step's barrier does not change that stage).
       if (!kSkip || keep_b[1])
-        bmm2_block(vs, 1, pb[1], qv_even);
+        bmm2_block(vs, 1, pb[1], qv_even, kpre(kst(IC<(S + 1) & 3>{}), 1));
       else
-        valu_block(qv_even);
+        valu_block(qv_even, kpre(kst(IC<(S + 1) & 3>{}), 1));
       keep_b[0] = q_check(sb[0], pb[0], 2 * j + 2);
     }
   };
