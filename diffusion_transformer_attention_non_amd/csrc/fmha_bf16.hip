@@ -101,7 +101,9 @@ __device__ __forceinline__ int key_of_mfma_row(int i) {
 //      physical 16-byte chunk = logical chunk ^ (r & 15);
 //   V: row = key, physical 64-byte segment = logical segment ^ (key & 3).
 
-template <bool kSkip>
+// kBitmap (with kSkip): the caller asked for the per-half skip bitmap; the
+// common case has no store in the loop at all.
+template <bool kSkip, bool kBitmap>
 __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
   const int nvote = (Skv + kSkipBlockN - 1) / kSkipBlockN;
   const bool qv0 = q0 + l32 < Sq, qv1 = q0 + 32 + l32 < Sq;
   uint8_t* bitmap_row = nullptr;
-  if (kSkip && p.bitmap != nullptr && q0 < Sq)
+  if (kBitmap && p.bitmap != nullptr && q0 < Sq)
     bitmap_row = p.bitmap + ((int64_t)(b * p.Hq + h) * ((Sq + kSkipBlockM - 1) / kSkipBlockM) + q0 / kSkipBlockM) * nvote;
   // After the Q block of half u: vote (kSkip), then move the reference if a
   // kept half's maximum passed the slack.  Returns whether half u is kept.
@@ -433,17 +435,19 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
     float mx[2];
     finish_max(mx);
     if constexpr (kSkip) {
-      bool keep = false;   // halves past S_kv hold no keys: nothing to vote on or to add
-      if (u < nvote) {
-        // Past the first half every valid row has a finite running maximum
-        // and a finite half maximum, so >= is the negation of <.  Bitwise
-        // operators keep the vote free of branches.
-        const float mxh = hh ? mx[1] : mx[0];
-        const bool hot = (hh ? qv1 : qv0) & (mxh - mrun >= p.log2_lambda);
-        keep = u == 0 || __any(hot);
-        if (bitmap_row != nullptr && lane == 0) bitmap_row[u] = keep ? 0 : 1;
-        if (!keep) ++skipped;
+      // Past the first half every valid row has a finite running maximum
+      // and a finite half maximum, so >= is the negation of <.  The vote is
+      // scalar arithmetic on wavefront-uniform values with one branch (on
+      // keep): with one wavefront per SIMD every taken branch is lost time.
+      // Halves past S_kv hold no keys: not kept, not counted.
+      const float mxh = hh ? mx[1] : mx[0];
+      const bool hot = (hh ? qv1 : qv0) & (mxh - mrun >= p.log2_lambda);
+      const bool in_range = u < nvote;
+      const bool keep = in_range & ((u == 0) | __any(hot));
+      if constexpr (kBitmap) {
+        if (bitmap_row != nullptr && in_range && lane == 0) bitmap_row[u] = keep ? 0 : 1;
       }
+      skipped += (unsigned)(in_range & !keep);
       if (!keep) {
         asm volatile("");
         return false;
@@ -451,9 +455,9 @@ __global__ __launch_bounds__(kDenseWaves * 64, 1) void fmha_bf16_kernel(FmhaBf16
       // Keeps the compiler from hoisting the next BMM2 block's operand reads
       // above the vote (they would stay live through it).
       asm volatile("" ::: "memory");
-      mrun = max_raw(mrun, hh ? mx[1] : mx[0]);
+      mrun = max_raw(mrun, mxh);
     }
-    if (needs_rescale(mx)) {
+    if (__builtin_expect(needs_rescale(mx), 0)) {   // rare: laid out off the fall-through path
       rescale(mx);
       redo_q_pairs(sv, pout);
     }
@@ -586,7 +590,7 @@ hipError_t launch_fmha_bf16(const FmhaBf16Args& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
   const int64_t nwg = nqt * a.Hq * a.B;
   if (nwg <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fmha_bf16_kernel<false>, dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((fmha_bf16_kernel<false, false>), dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -594,7 +598,10 @@ hipError_t launch_fmha_bf16_skip(const FmhaBf16Args& a, hipStream_t stream) {
   const int64_t nqt = (a.Sq + kBlockM - 1) / kBlockM;
   const int64_t nwg = nqt * a.Hq * a.B;
   if (nwg <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fmha_bf16_kernel<true>, dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
+  if (a.bitmap != nullptr)
+    hipLaunchKernelGGL((fmha_bf16_kernel<true, true>), dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fmha_bf16_kernel<true, false>), dim3((unsigned)nwg), dim3(kDenseWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

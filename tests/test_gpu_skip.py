@@ -39,6 +39,24 @@ def test_factor_zero_is_bit_identical_to_dense():
     assert int(ex["bitmap"].sum()) == 0 and int(ex["skipped"][0]) == 0
 
 
+@pytest.mark.parametrize("factor", [1.0, 100.0])
+def test_bitmap_and_count_do_not_change_the_output(factor):
+    """Asking for the bitmap selects another kernel instantiation (the common
+    case has no store in its loop): outputs, and LSE, must not depend on it."""
+    announce(f"skip output with and without bitmap, factor={factor}")
+    q, k, v = positional_qkv(grid=(3, 9, 17), H=3, seed=4)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    plain, ex0 = dit.attn_skip_softmax(qd, kd, vd, factor, return_lse=True)
+    counted, ex1 = dit.attn_skip_softmax(qd, kd, vd, factor, return_count=True, return_lse=True)
+    mapped, ex2 = dit.attn_skip_softmax(qd, kd, vd, factor, return_bitmap=True, return_count=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, counted) and torch.equal(plain, mapped)
+    assert torch.equal(ex0["lse"], ex1["lse"]) and torch.equal(ex0["lse"], ex2["lse"])
+    assert int(ex1["skipped"][0]) == int(ex2["skipped"][0]) == int(ex2["bitmap"].sum())
+    if factor >= 100.0:
+        assert int(ex2["skipped"][0]) > 0
+
+
 @pytest.mark.parametrize("grid,H,factor", [((2, 8, 24), 2, 1.0), ((2, 8, 24), 2, 10.0), ((2, 8, 24), 2, 100.0),
                                            ((3, 9, 17), 3, 30.0), ((1, 1, 200), 2, 50.0)])
 def test_skip_set_and_output_match_oracle(grid, H, factor):
