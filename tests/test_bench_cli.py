@@ -26,7 +26,7 @@ def test_traffic_record_is_for_the_dense_kernel():
     sys.path.insert(0, ROOT)
     import bench
     rec = json.load(open(bench.TRAFFIC_FILE))
-    assert "fmha_bf16_kernel<false>" in rec["kernel"]
+    assert "fmha_bf16_kernel<false, false>" in rec["kernel"]
     assert rec["hbm_bytes_per_launch"] > rec["algorithmic_bytes_per_launch"] > 0
     t = bench.traffic_for_current_kernel()
     assert t is None or t == rec["hbm_bytes_per_launch"]
