@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the factor sweep")
     ap.add_argument("--profile-call", choices=PROFILE_CALLS, default=None,
                     help="run only this attention call (warmup + steps launches) for counter collection")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="print the VALU issue-rate and MFMA/VALU co-execution probes as one JSON line and exit")
     return ap.parse_args()
 
 
@@ -145,6 +147,62 @@ def mfma_peak_probe(torch):
                      "mfma": {0: "v_mfma_f32_32x32x16_bf16", 1: "v_mfma_f32_32x32x64_f8f6f4",
                               2: "v_mfma_i32_32x32x32_i8"}[kind]}
     return out
+
+
+ISSUE_VALU_KINDS = ("v_add_f32", "v_fma_f32", "v_max3_f32", "v_exp_f32", "v_cvt_pk_fp8_f32", "v_pk_fma_f16")
+ISSUE_COEXEC_MODES = (
+    ("mfma_only", "per wavefront one E4M3 32x32x64 MFMA (four independent accumulators)"),
+    ("split", "half the wavefronts one MFMA, the other half 16 v_fma_f32 (2 wavefronts per SIMD)"),
+    ("fma16_after_each_mfma", "one MFMA, then 16 independent v_fma_f32 of the same wavefront"),
+    ("softmax_mix_after_each_mfma", "one MFMA, then four logits: fma -> exp2, sum, 2 max3, 2 E4M3 packs"),
+    ("softmax_mix_burst", "the same work as four MFMAs followed by four logit groups"),
+)
+
+
+def issue_probe(torch):
+    """Instruction-issue probes (csrc/issue_probe.hip), one workgroup per CU
+    with 1-3 wavefronts per SIMD, each wavefront timing its loop with the
+    shader cycle counter; reports the slowest wavefront's span per unit."""
+    import ctypes
+    path = os.path.join(ROOT, "diffusion_transformer_attention_non_amd", "libditattn_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.issue_probe_launch.restype = ctypes.c_int
+    lib.issue_probe_launch.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def span(probe, kind, wps, iters):
+        waves = cus * 4 * wps
+        cycles = torch.zeros(waves, dtype=torch.int64, device="cuda")
+        sink = torch.zeros(waves * 64, dtype=torch.float32, device="cuda")
+        for it in (8, iters):   # a short warm-up launch, then the timed one
+            rc = lib.issue_probe_launch(probe, kind, wps, cus, it, cycles.data_ptr(), sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"issue_probe_launch({probe}, {kind}, {wps}) returned {rc}")
+        torch.cuda.synchronize()
+        return float(cycles.max().item())
+
+    valu = {}
+    for kind, name in enumerate(ISSUE_VALU_KINDS):
+        iters = 4000
+        valu[name] = {f"{w}_waves_per_simd": span(0, kind, w, iters) / (iters * lib.issue_probe_per_iter(0) * w)
+                      for w in (1, 2, 3)}
+    coexec = {}
+    for mode, (name, what) in enumerate(ISSUE_COEXEC_MODES):
+        iters = 2000
+        rows, per_mfma = {}, {}
+        for w in ((2,) if name == "split" else (1, 2, 3)):
+            rows[f"{w}_waves_per_simd"] = span(1, mode, w, iters) / (iters * lib.issue_probe_per_iter(1))
+            if name != "split":   # every wavefront issues one MFMA per step
+                per_mfma[f"{w}_waves_per_simd"] = rows[f"{w}_waves_per_simd"] / w
+        coexec[name] = {"step": what, "simd_cycles_per_step": rows}
+        if per_mfma:
+            coexec[name]["simd_cycles_per_mfma"] = per_mfma
+    return {"probe": "instruction issue (csrc/issue_probe.hip)", "cus": cus,
+            "valu_simd_cycles_per_wavefront_instruction": valu,
+            "mfma_valu_coexecution": coexec,
+            "note": "a step is per wavefront; with w wavefronts per SIMD the SIMD runs w steps in the span, "
+                    "so an E4M3 MFMA alone costs 64 * w cycles per step at the full rate"}
 
 
 def cpu_baseline(budget_s, S, H, step_flops):
@@ -332,6 +390,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.profile_call:
         profile_call(args, dit, generate, torch, dev)
+        return
+    if args.issue_probe:
+        print(json.dumps(issue_probe(torch)), flush=True)
         return
     B, S, H, D = WAN["B"], WAN["S"], WAN["H"], WAN["D"]
     print(f"[bench] generating Wan-shaped inputs B={B} S={S} H={H} D={D}", file=sys.stderr, flush=True)

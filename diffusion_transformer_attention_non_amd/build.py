@@ -15,9 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libditattn.so")
 SOURCES = ["abi.hip", "fmha_bf16.hip", "fmha_sage.hip", "sage_quant.hip"]
-# The benchmark's matrix-core peak probe: its own shared object, outside the library's interface.
+# The benchmark's matrix-core peak and instruction-issue probes: their own
+# shared object, outside the library's interface.
 PROBE_LIB = os.path.join(PKG, "libditattn_probe.so")
-PROBE_SOURCES = ["mfma_probe.hip"]
+PROBE_SOURCES = ["mfma_probe.hip", "issue_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
