@@ -9,9 +9,9 @@ namespace ditattn {
 // Tile geometry shared by the attention kernels and the host layer.
 constexpr int kHeadDim = 128;
 constexpr int kWaveRows = 32;    // query rows per wavefront in the low-precision (SAGE) kernel,
-                                  // its Skip-Softmax vote rows
-constexpr int kWavesPerWG = 8;   // two wavefronts per SIMD
-constexpr int kBlockM = kWaveRows * kWavesPerWG;  // query rows per workgroup (every kernel)
+                                  // its Skip-Softmax vote rows (its workgroup: 12 wavefronts, 384 rows)
+constexpr int kBlockM = 256;      // query rows per workgroup of the BF16 kernels (4 wavefronts x 64),
+                                  // the most workgroups any attention launch uses per head
 constexpr int kBlockN = 64;       // keys per KV tile (LDS stage)
 constexpr int kSkipBlockM = 64;   // BF16 kernels: query rows per wavefront = rows per Skip-Softmax vote
 constexpr int kSkipBlockN = 32;   // keys per BF16 Skip-Softmax vote (half a KV tile)
