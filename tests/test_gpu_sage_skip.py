@@ -42,7 +42,8 @@ def test_factor_zero_is_bit_identical_to_sage(dt, qb, kb):
 
 CASES = [((2, 8, 24), 2, 2, "int8", 1, 16, 1.0), ((2, 8, 24), 2, 2, "fp8", 1, 4, 10.0),
          ((2, 8, 24), 2, 2, "fp8", 1, 1, 100.0), ((3, 9, 17), 4, 2, "int8", 4, 1, 30.0),
-         ((1, 1, 200), 2, 1, "fp8", 16, 16, 50.0)]
+         ((1, 1, 200), 2, 1, "fp8", 16, 16, 50.0),
+         ((3, 8, 24), 2, 2, "fp8", 1, 4, 1000.0)]   # lambda = 1000 / 576 > 1
 
 
 @pytest.mark.parametrize("grid,Hq,Hkv,dt,qb,kb,factor", CASES)

@@ -58,7 +58,10 @@ def test_bitmap_and_count_do_not_change_the_output(factor):
 
 
 @pytest.mark.parametrize("grid,H,factor", [((2, 8, 24), 2, 1.0), ((2, 8, 24), 2, 10.0), ((2, 8, 24), 2, 100.0),
-                                           ((3, 9, 17), 3, 30.0), ((1, 1, 200), 2, 50.0)])
+                                           ((3, 9, 17), 3, 30.0), ((1, 1, 200), 2, 50.0),
+                                           # factor above S_kv: lambda = 1000 / 576 > 1, so a half is kept
+                                           # only where its maximum rises past the running maximum
+                                           ((3, 8, 24), 2, 1000.0)])
 def test_skip_set_and_output_match_oracle(grid, H, factor):
     announce(f"skip grid={grid} H={H} factor={factor}")
     bm, bn = dit.tile_config()
